@@ -1,0 +1,193 @@
+"""fp64 CPU oracle of the Kimi Delta Attention recurrence (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: tests/, the smoke check and the bench's CPU-baseline
+leg may import this package; the library under ``gated_delta_rule_88_amd/``
+never does, and nothing here imports that package.
+
+The arithmetic lives in ``kda_oracle.c`` (token-by-token recurrence of the
+page "Kimi Delta Attention", §03, with the read-out of §02).  This module only
+compiles it with gcc on first use, marshals arrays and exposes two calls:
+
+* :func:`prefill` -- varlen packed sequences, optional initial state, returns
+  outputs and final states;
+* :func:`decode_step` -- one token per (sequence, head): exactly one loop
+  iteration of the same recurrence (the "fused recurrent" decode mode of §06).
+
+Inputs may be numpy arrays or torch CPU tensors in float64, float32 or
+bfloat16; they are converted to fp64 exactly inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libkda_oracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+MODE_KDA, MODE_ERASE_OFF = 0, 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH, force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, -O2, no fast-math) into ``out``."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        p = path or build()
+        lib = ctypes.CDLL(p)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.kda_oracle_prefill.restype = i32
+        lib.kda_oracle_prefill.argtypes = [
+            vp, vp, vp, vp, vp,      # q k v log_alpha beta
+            i32, i32,                # in_type la_type
+            vp, i32,                 # cu_seqlens num_seqs
+            vp, vp,                  # init_state o
+            vp, i64,                 # out_rows n_out_rows
+            vp,                      # final_state
+            i32, i32, i32, i32, i32  # H dk dv mode nthreads
+        ]
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _typed(x, allow=(F32, BF16, F64)):
+    """Return (contiguous numpy array keeping memory alive, type code)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            t = x.detach().to("cpu").contiguous()
+            if t.dtype == torch.bfloat16:
+                arr, code = t.view(torch.int16).numpy().view(np.uint16), BF16
+            elif t.dtype == torch.float32:
+                arr, code = t.numpy(), F32
+            elif t.dtype == torch.float64:
+                arr, code = t.numpy(), F64
+            else:
+                raise TypeError(f"unsupported tensor dtype {t.dtype}")
+            if code not in allow:
+                raise TypeError(f"dtype {t.dtype} not allowed here")
+            return np.ascontiguousarray(arr), code
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.float64:
+        code = F64
+    elif a.dtype == np.float32:
+        code = F32
+    elif a.dtype == np.uint16:
+        code = BF16  # raw bfloat16 bit patterns
+    else:
+        raise TypeError(f"unsupported array dtype {a.dtype}")
+    if code not in allow:
+        raise TypeError(f"dtype {a.dtype} not allowed here")
+    return a, code
+
+
+def _f64(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
+            out_rows=None, mode: int = MODE_KDA, nthreads: int | None = None,
+            want_final: bool = True, lib=None):
+    """Run the recurrence over packed sequences.
+
+    Shapes: q, k ``[T,H,dk]``; v ``[T,H,dv]``; log_alpha ``[T,H,dk]``; beta
+    ``[T,H]``; cu_seqlens ``[N+1]``; init_state ``[N,H,dv,dk]`` (stored as
+    S^T, key index last) or None.  q, k, v and beta must share one dtype.
+
+    Returns ``(o, final_state)`` as float64 arrays: o is ``[T,H,dv]`` (or
+    ``[len(out_rows),H,dv]``), final_state ``[N,H,dv,dk]`` (None when
+    ``want_final`` is False).
+    """
+    lib = lib or load()
+    qa, tq = _typed(q)
+    ka, tk = _typed(k)
+    va, tv = _typed(v)
+    ba, tb = _typed(beta)
+    if not (tq == tk == tv == tb):
+        raise TypeError("q, k, v and beta must share one dtype")
+    la, tla = _typed(log_alpha, allow=(F32, F64))
+    T, H, dk = qa.shape
+    dv = va.shape[-1]
+    if ka.shape != (T, H, dk) or la.shape != (T, H, dk) or va.shape != (T, H, dv) or ba.shape != (T, H):
+        raise ValueError("inconsistent input shapes")
+    cu = np.ascontiguousarray(np.asarray(
+        cu_seqlens.cpu().numpy() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if N < 0 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    s0 = _f64(init_state)
+    if s0 is not None and s0.shape != (N, H, dv, dk):
+        raise ValueError("init_state must be [N,H,dv,dk]")
+    rows = None
+    if out_rows is not None:
+        rows = np.ascontiguousarray(np.asarray(out_rows, dtype=np.int64))
+        if rows.ndim != 1 or np.any(np.diff(rows) <= 0) or (rows.size and (rows[0] < 0 or rows[-1] >= T)):
+            raise ValueError("out_rows must be strictly increasing token indices")
+    n_rows = T if rows is None else rows.shape[0]
+    o = np.zeros((n_rows, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dv, dk), dtype=np.float64) if want_final else None
+    rc = lib.kda_oracle_prefill(
+        _ptr(qa), _ptr(ka), _ptr(va), _ptr(la), _ptr(ba), tq, tla,
+        _ptr(cu), N, _ptr(s0), _ptr(o), _ptr(rows), 0 if rows is None else rows.shape[0],
+        _ptr(fin), H, dk, dv, mode, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill failed with code {rc}")
+    return o, fin
+
+
+def decode_step(q, k, v, log_alpha, beta, state, *, nthreads: int | None = None, lib=None):
+    """One recurrent step for N sequences x H heads.
+
+    q, k ``[N,H,dk]``; v ``[N,H,dv]``; log_alpha ``[N,H,dk]``; beta ``[N,H]``;
+    state ``[N,H,dv,dk]``.  Returns ``(o [N,H,dv], new_state [N,H,dv,dk])``;
+    the input state is not modified.
+    """
+    qa, _ = _typed(q)
+    N = qa.shape[0]
+    cu = np.arange(N + 1, dtype=np.int64)
+    return prefill(q, k, v, log_alpha, beta, cu, state, nthreads=nthreads, lib=lib)
