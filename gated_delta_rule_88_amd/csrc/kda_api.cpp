@@ -1,0 +1,95 @@
+// kda_api.cpp -- the C ABI of include/kda.h: host-side validation (no HIP
+// call happens before every check has passed), workspace sizing, and the
+// hand-off to the kernel launchers.
+#include "kda.h"
+
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_common(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv,
+                        kda_dtype dtype) {
+  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+  if (num_seqs < 0 || num_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+  if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head size (dk == dv in {64, 128} required)";
+    case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_DTYPE: return "unknown element type";
+    case KDA_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int kda_version(void) { return 100; }  // 0.1.0
+
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                  int32_t dk, int32_t dv, kda_dtype dtype) {
+  if (check_common(num_seqs, num_heads, dk, dv, dtype) != KDA_OK) return 0;
+  if (total_tokens < 0 || total_tokens > INT32_MAX) return 0;
+  const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
+  return (size_t)slots * (size_t)num_heads * kda::prefill_record_bytes(dk, dtype == KDA_BF16);
+}
+
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const void* beta,
+                              const int32_t* cu_seqlens, const float* init_state,
+                              void* o, float* final_state, int32_t num_seqs,
+                              int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                              kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const size_t need = kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype);
+  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+  a.cu_seqlens = cu_seqlens; a.init_state = init_state; a.o = o; a.final_state = final_state;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.num_heads = num_heads; a.d = dk;
+  a.bf16 = dtype == KDA_BF16; a.workspace = workspace;
+  return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const void* beta, float* state, void* o, int32_t num_seqs,
+                           int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                           hipStream_t stream) {
+  kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_SHAPE;
+  if (num_seqs == 0) return KDA_OK;
+  if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, state, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.state = state; a.o = o;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.d = dk; a.bf16 = dtype == KDA_BF16;
+  return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// kda_decode.hip -- one recurrent KDA step per (sequence, head), in place.
+//
+// Operation (page "Kimi Delta Attention", §03 recurrence with the §02
+// read-out; §06 "fused recurrent KDA": consume one q/k/v and gate set,
+// decay, correct and write the state in place, read a fixed amount of
+// recurrent memory).  With the state stored as S^T (row j = value channel j,
+// key index i contiguous) and alpha = exp(log_alpha):
+//
+//   p_j   = sum_i S_ij alpha_i k_i          read of the decayed state at k
+//   r_j   = sum_i S_ij alpha_i q_i          decayed state read at q
+//   e_j   = beta (v_j - p_j)                scaled error
+//   S_ij <- alpha_i S_ij + k_i e_j          decay + correction, in place
+//   o_j   = r_j + (k . q) e_j               = (S_new^T q)_j
+//
+// Memory plan (HBM-bound: 2 x 64 KiB of state per head against 1.5 KiB of
+// token data): one workgroup of 256 threads per (sequence, head).  Sixteen
+// lanes own one state row at a time, each lane D/16 keys as float4 pieces,
+// so every load and store instruction of a wave moves four contiguous
+// 256-byte row segments.  A thread issues all of its row loads before any
+// arithmetic (16 float4 in flight per lane at D = 128).  The two dot
+// products reduce over the 16 lanes of a DPP row; no LDS and no barrier.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <class P, int D>
+__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+    const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
+    const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
+    const typename P::In* __restrict__ beta, float* __restrict__ state,
+    typename P::In* __restrict__ o) {
+  using In = typename P::In;
+  constexpr int NK = D / 16;        // keys per lane
+  constexpr int NC = NK / 4;        // float4 pieces per lane and row
+  constexpr int ROWS = D / 16;      // rows per 16-lane group
+
+  const int64_t tok = blockIdx.x;   // n * H + h
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;         // 16 groups of 16 lanes
+  const int l16 = tid & 15;
+
+  // token vectors for this lane's keys: c * 64 + 4 * l16 + {0..3}
+  float a[NK], kk[NK], aq[NK], ak[NK];
+  float kq_part = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int64_t base = tok * D + c * 64 + 4 * l16;
+    const f32x4 la = *reinterpret_cast<const f32x4*>(log_alpha + base);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ai = __expf(la[e]);
+      const float ki = to_f32(k[base + e]);
+      const float qi = to_f32(q[base + e]);
+      a[4 * c + e] = ai;
+      kk[4 * c + e] = ki;
+      ak[4 * c + e] = ai * ki;
+      aq[4 * c + e] = ai * qi;
+      kq_part += ki * qi;
+    }
+  }
+  const float kq = row16_sum(kq_part);
+  const float b = to_f32(beta[tok]);
+
+  float* srow0 = state + tok * D * D;
+  f32x4 s[ROWS][NC];
+#pragma unroll
+  for (int it = 0; it < ROWS; ++it) {
+    const int j = grp * ROWS + it;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      s[it][c] = *reinterpret_cast<const f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16);
+  }
+
+  float my_o = 0.f;
+#pragma unroll
+  for (int it = 0; it < ROWS; ++it) {
+    const int j = grp * ROWS + it;
+    float pp = 0.f, rr = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp += s[it][c][e] * ak[4 * c + e];
+        rr += s[it][c][e] * aq[4 * c + e];
+      }
+    pp = row16_sum(pp);
+    rr = row16_sum(rr);
+    const float err = b * (to_f32(v[tok * D + j]) - pp);
+    const float oj = rr + kq * err;
+    if (l16 == it) my_o = oj;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      f32x4 ns;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ns[e] = a[4 * c + e] * s[it][c][e] + kk[4 * c + e] * err;
+      *reinterpret_cast<f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16) = ns;
+    }
+  }
+  if (l16 < ROWS) o[tok * D + grp * ROWS + l16] = from_f32<In>(my_o);
+}
+
+template <class P, int D>
+static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+  using In = typename P::In;
+  const unsigned blocks = (unsigned)((int64_t)A.num_seqs * A.num_heads);
+  hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kThreads), 0, stream,
+                     (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
+                     (const In*)A.beta, A.state, (In*)A.o);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& A, hipStream_t stream) {
+  if (A.num_seqs == 0) return hipSuccess;
+  if (A.bf16) return A.d == 128 ? launch_decode_t<PathBF16, 128>(A, stream)
+                                : launch_decode_t<PathBF16, 64>(A, stream);
+  return A.d == 128 ? launch_decode_t<PathF32, 128>(A, stream)
+                    : launch_decode_t<PathF32, 64>(A, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,44 @@
+// kda_launch.h -- host-side launch interface between the validated C ABI
+// (kda_api.cpp) and the kernels.  Arguments arrive here already checked.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float* log_alpha;
+  const void* beta;
+  float* state;
+  void* o;
+  int32_t num_seqs, num_heads, d;
+  bool bf16;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float* log_alpha;
+  const void* beta;
+  const int32_t* cu_seqlens;
+  const float* init_state;
+  void* o;
+  float* final_state;
+  int32_t num_seqs;
+  int64_t total_tokens;
+  int32_t num_heads, d;
+  bool bf16;
+  void* workspace;
+};
+
+// Per-chunk factor record of the prefill (bytes), and the number of chunk
+// slots reserved for (num_seqs, total_tokens).
+size_t prefill_record_bytes(int d, bool bf16);
+int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace kda

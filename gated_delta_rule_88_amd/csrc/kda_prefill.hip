@@ -1,0 +1,519 @@
+// kda_prefill.hip -- chunk-parallel KDA prefill over packed varlen sequences.
+//
+// The recurrence (page "Kimi Delta Attention", §03)
+//     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t
+// is evaluated in chunks of C = 64 tokens (§06 "chunk-parallel KDA": matrix
+// products inside a block, only the final state crosses block boundaries;
+// the "Kimi Linear Guide" page's hardware-chunking section uses B = 64).
+// The pages give the outline only; the chunk equations below follow from the
+// recurrence by unrolling it over one chunk.  For a chunk with tokens
+// r = 0..C-1 (a partial chunk is padded with k = q = v = 0, beta = 0,
+// log_alpha = 0, which leaves every result unchanged) and entering state S0:
+//
+//   G[r,i]  = sum_{s<=r} log_alpha[s,i]          cumulative log decay (fp32)
+//   Kg = K * e^G      Qg = Q * e^G      Kc = K * e^(G[C-1] - G)
+//   A[r,j]  = sum_i k_r[i] k_j[i] e^(G[r,i]-G[j,i])   for j < r, else 0
+//   Bqk[r,j]= sum_i q_r[i] k_j[i] e^(G[r,i]-G[j,i])   for j <= r, else 0
+//   T       = (I + Diag(beta) A)^-1      (unit lower triangular)
+//   W = T Diag(beta) Kg          U = T Diag(beta) V
+//   E       = U - W S0           row r = beta_r (v_r - (Diag(a_r) S_{r-1})^T k_r)
+//   O       = Qg S0 + Bqk E
+//   S_end   = Diag(e^G[C-1]) S0 + Kc^T E
+//
+// The decays e^(G[r]-G[j]) inside A and Bqk are formed as a product of two
+// factors anchored at token m = 31, X = e^(G - G[m]) and 1/X, so that no
+// factor leaves the fp32 range for |log_alpha| <= 2.5 (the numerical-range
+// concern of §08 item 3).
+//
+// Kernel 1 (prep, one workgroup per chunk and head, all chunks in parallel)
+// computes G, A, Bqk, T, W, U, Qg, Kc and writes them to the workspace as
+// MFMA operand fragments (see kda_device.h for the fragment map).
+// Kernel 2 (state pass, one workgroup per (sequence, head, 16 value
+// columns)) walks the chunks of its sequence in order with its 128 x 16
+// slice of S resident in accumulator registers: value columns of S never mix
+// in the recurrence, so the slices are independent.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------------------
+// Per (chunk slot, head) record in the workspace.
+// ---------------------------------------------------------------------------
+template <class P, int D>
+struct Rec {
+  static constexpr int ES = sizeof(typename P::In);
+  static constexpr int KB = D / 32;                 // 32-deep key blocks
+  static constexpr int NT = D / 16;                 // 16-wide key / value tiles
+  static constexpr size_t FB = 64 * 8 * ES;         // bytes per fragment
+  static constexpr size_t W = 0;                    // [4 token tiles][KB]   W   (row token, k key)
+  static constexpr size_t Q = W + 4 * KB * FB;      // [4][KB]               Qg  (row token, k key)
+  static constexpr size_t KC = Q + 4 * KB * FB;     // [NT key tiles][2]     Kc^T (row key, k token)
+  static constexpr size_t B = KC + NT * 2 * FB;     // [4 token tiles][2]    Bqk (row token, k token)
+  static constexpr size_t U = B + 8 * FB;           // [NT value tiles][4 token tiles][64] f32x4
+  static constexpr size_t G = U + (size_t)NT * 4 * 64 * 16;  // [D] fp32 e^G[C-1]
+  static constexpr size_t BYTES = G + (size_t)D * 4;
+};
+
+size_t prefill_record_bytes(int d, bool bf16) {
+  if (d == 128) return bf16 ? Rec<PathBF16, 128>::BYTES : Rec<PathF32, 128>::BYTES;
+  return bf16 ? Rec<PathBF16, 64>::BYTES : Rec<PathF32, 64>::BYTES;
+}
+
+// Chunk slots: chunk c of sequence n lives in slot cu[n]/64 + n + c.  Slots
+// of different sequences never collide (floor(a/64) + ceil(L/64) <=
+// floor((a+L)/64) + 1), and every slot is below T/64 + N + 1.
+int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens) {
+  return total_tokens / kChunk + num_seqs + 1;
+}
+
+__device__ __forceinline__ int64_t slot_key(const int32_t* cu, int n) {
+  return (int64_t)(cu[n] / kChunk) + n;
+}
+
+// slot -> (sequence, first token, length); false for an unused slot.
+__device__ __forceinline__ bool decode_slot(const int32_t* __restrict__ cu, int N, int64_t slot,
+                                            int& n, int64_t& t0, int& len) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_key(cu, mid) <= slot) lo = mid; else hi = mid - 1;
+  }
+  n = lo;
+  const int64_t c = slot - slot_key(cu, lo);
+  const int64_t L = (int64_t)cu[lo + 1] - cu[lo];
+  if (c < 0 || c * kChunk >= L) return false;
+  t0 = cu[lo] + c * kChunk;
+  len = (int)min<int64_t>(kChunk, L - c * kChunk);
+  return true;
+}
+
+// four consecutive inputs of a token-major LDS row as fp32
+__device__ __forceinline__ f32x4 lds4(const __bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Kernel 1: per-chunk factors
+// ---------------------------------------------------------------------------
+template <class P, int D>
+__global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
+    const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
+    const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
+    const typename P::In* __restrict__ beta, const int32_t* __restrict__ cu, int N, int H,
+    unsigned char* __restrict__ ws) {
+  using In = typename P::In;
+  using Frag = typename P::Frag;
+  using Half = typename P::Half;
+  using R = Rec<P, D>;
+  constexpr int C = kChunk;
+  constexpr int PI = D + 16 / (int)sizeof(In) * 1;  // row pitch of staged inputs (+16 bytes)
+  constexpr int PX = D + 4;                          // row pitch of X
+  constexpr int PL = C + 4;                          // row pitch of L and T
+  constexpr int KB = D / 32, NT = D / 16;
+  constexpr int QBYTES = (C * PI * (int)sizeof(In)) > (C * PL * 4) ? (C * PI * (int)sizeof(In)) : (C * PL * 4);
+
+  __shared__ __align__(16) In sK[C][PI];
+  __shared__ __align__(16) In sV[C][PI];
+  __shared__ __align__(16) unsigned char sQraw[QBYTES];   // Q, later T
+  __shared__ __align__(16) float sX[C][PX];               // e^(G - G[m])
+  __shared__ __align__(16) float sL[C][PL];               // Diag(beta) A (strictly lower)
+  __shared__ float sEgm[D], sEcm[D], sGm[D], sGc[D], sBeta[C];
+  __shared__ float sSeg[4][D];
+  __shared__ float sScr[4][16][17];
+  In (*sQ)[PI] = reinterpret_cast<In (*)[PI]>(sQraw);
+  float (*sT)[PL] = reinterpret_cast<float (*)[PL]>(sQraw);
+
+  const int64_t slot = blockIdx.x;
+  const int h = blockIdx.y;
+  int n, len;
+  int64_t t0;
+  if (!decode_slot(cu, N, slot, n, t0, len)) return;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
+  unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
+
+  // ---- phase 1: stage K, Q, V rows, beta; clear L -------------------------
+  {
+    constexpr int EV = 16 / (int)sizeof(In);  // elements per 16-byte vector
+    constexpr int VR = D / EV;                // vectors per row
+    for (int idx = tid; idx < C * VR; idx += kThreads) {
+      const int r = idx / VR, cv = idx % VR;
+      uint4 kq = {0, 0, 0, 0}, qq = {0, 0, 0, 0}, vq = {0, 0, 0, 0};
+      if (r < len) {
+        const int64_t off = ((t0 + r) * H + h) * D + cv * EV;
+        kq = *reinterpret_cast<const uint4*>(k + off);
+        qq = *reinterpret_cast<const uint4*>(q + off);
+        vq = *reinterpret_cast<const uint4*>(v + off);
+      }
+      *reinterpret_cast<uint4*>(&sK[r][cv * EV]) = kq;
+      *reinterpret_cast<uint4*>(&sQ[r][cv * EV]) = qq;
+      *reinterpret_cast<uint4*>(&sV[r][cv * EV]) = vq;
+    }
+    if (tid < C) sBeta[tid] = tid < len ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+    for (int idx = tid; idx < C * PL; idx += kThreads) (&sL[0][0])[idx] = 0.f;
+  }
+
+  // ---- phase 2: cumulative log decay and the anchored factor X -------------
+  {
+    constexpr int SEGS = kThreads / D;   // token segments per channel
+    constexpr int SL = C / SEGS;         // tokens per segment
+    const int i = tid % D, s = tid / D;
+    float gl[SL];
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < SL; ++r) {
+      const int tok = s * SL + r;
+      const float x = tok < len ? log_alpha[((t0 + tok) * H + h) * D + i] : 0.f;
+      run += x;
+      gl[r] = run;
+    }
+    sSeg[s][i] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = 0; s2 < s; ++s2) off += sSeg[s2][i];
+#pragma unroll
+    for (int r = 0; r < SL; ++r) gl[r] += off;
+    constexpr int M = 31;
+    if (s == M / SL) sGm[i] = gl[M % SL];
+    if (s == SEGS - 1) sGc[i] = gl[SL - 1];
+    __syncthreads();
+    const float gm = sGm[i], gc = sGc[i];
+#pragma unroll
+    for (int r = 0; r < SL; ++r) sX[s * SL + r][i] = __expf(gl[r] - gm);
+    if (s == 0) {
+      sEgm[i] = __expf(gm);
+      sEcm[i] = __expf(gc - gm);
+      reinterpret_cast<float*>(rec + R::G)[i] = __expf(gc);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: A and Bqk^T tiles (MFMA), Qg fragments ----------------------
+  {
+    // fragment of a token-major operand: row `row`, key block p, times X or 1/X
+    auto row_frag = [&](const In (*src)[PI], int row, int p, bool inv, float (&vals)[8]) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = 32 * p + 16 * hh + 4 * g;
+        const f32x4 a = lds4(&src[row][key]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sX[row][key]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[4 * hh + e] = inv ? a[e] / x[e] : a[e] * x[e];
+      }
+    };
+    for (int pi = w; pi < 10; pi += 4) {
+      // lower-triangular tile pairs (rt, jt), jt <= rt, in row order
+      const int rt = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+      const int jt = pi - (rt * (rt + 1)) / 2;
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        float va[8], vb[8], vq[8];
+        row_frag(sK, 16 * rt + l16, p, false, va);   // Ka: k_r e^(G_r - G_m)
+        row_frag(sK, 16 * jt + l16, p, true, vb);    // Kbar: k_j e^(G_m - G_j)
+        row_frag(sQ, 16 * rt + l16, p, false, vq);   // Qa: q_r e^(G_r - G_m)
+        const Split<P> ka = make_split<P>(va), kb = make_split<P>(vb), qa = make_split<P>(vq);
+        mma_ss<P>(accA, ka, kb);   // A[r][j]
+        mma_ss<P>(accB, kb, qa);   // Bqk^T[j][r]
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g + e, j = 16 * jt + l16;
+        sL[r][j] = (j < r) ? sBeta[r] * accA[e] : 0.f;
+      }
+      // Bqk fragment (row tile rt, token block jt/2): lane l holds rows
+      // r = 16 rt + l16 and columns j = 16 jt + 4 g + e
+      Half hb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * jt + 4 * g + e, r = 16 * rt + l16;
+        hb[e] = from_f32<In>(j <= r ? accB[e] : 0.f);
+      }
+      In* bfrag = reinterpret_cast<In*>(rec + R::B) + ((size_t)(rt * 2 + jt / 2) * 64 + l) * 8;
+      *reinterpret_cast<Half*>(bfrag + 4 * (jt & 1)) = hb;
+      if (jt == rt && (rt & 1) == 0) {
+        Half z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = from_f32<In>(0.f);
+        *reinterpret_cast<Half*>(bfrag + 4) = z;   // columns above the diagonal
+      }
+    }
+    // Qg fragments: token tile rt = w, all key blocks
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      float vq[8];
+      row_frag(sQ, 16 * w + l16, p, false, vq);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vq[m] *= sEgm[32 * p + kpos(g, m)];
+      *reinterpret_cast<Frag*>(rec + R::Q + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag)) = make_frag<P>(vq);
+    }
+  }
+  __syncthreads();   // Q is dead from here on: its space becomes T
+
+  // ---- phase 4: T = (I + Diag(beta) A)^-1 by blocked forward substitution --
+  {
+    for (int idx = tid; idx < C * PL; idx += kThreads) (&sT[0][0])[idx] = 0.f;
+    __syncthreads();
+    if (w == 0) {
+      // the four 16 x 16 diagonal blocks: lane = (block, column)
+      const int bk = l >> 4, c = l & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) acc -= sL[16 * bk + r][16 * bk + j] * x[j];
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[16 * bk + r][16 * bk + c] = x[r];
+    }
+    __syncthreads();
+    // off-diagonal blocks, one column block per wave:
+    //   T_ba = -T_bb * sum_{kb=a}^{b-1} L_b,kb T_kb,a
+    const int a = w, c = l16, rr0 = 4 * g;
+    for (int step = 1; step < 4; ++step) {
+      const int bb = a + step;
+      const bool act = bb < 4;
+      if (act) {
+        float tmp[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = a; kb < bb; ++kb)
+          for (int qq = 0; qq < 16; ++qq) {
+            const float tv = sT[16 * kb + qq][16 * a + c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tmp[e] += sL[16 * bb + rr0 + e][16 * kb + qq] * tv;
+          }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sScr[w][rr0 + e][c] = tmp[e];
+      }
+      __syncthreads();
+      if (act) {
+        float res[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int qq = 0; qq < 16; ++qq) {
+          const float tv = sScr[w][qq][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) res[e] -= sT[16 * bb + rr0 + e][16 * bb + qq] * tv;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[16 * bb + rr0 + e][16 * a + c] = res[e];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- phase 5: W^T = Kg^T T'^T and U = T' V with T' = T Diag(beta);
+  //               Kc^T fragments ---------------------------------------------
+  {
+    // T' fragments (row tile rt, token block p); used as the B operand of
+    // W^T and the A operand of U (the two layouts coincide)
+    Split<P> tf[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float vals[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int j = 32 * p + kpos(g, m);
+          vals[m] = sT[16 * rt + l16][j] * sBeta[j];
+        }
+        tf[rt][p] = make_split<P>(vals);
+      }
+    constexpr int TPW = NT / 4;   // key (and value) tiles per wave
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int it = w * TPW + tt;        // key tile for W and Kc, value tile for U
+      const int col = 16 * it + l16;
+      Split<P> kg[2];
+      Frag vf[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float vg[8], vc[8], vv[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int j = 32 * p + kpos(g, m);
+          const float kx = to_f32(sK[j][col]);
+          const float x = sX[j][col];
+          vg[m] = kx * x * sEgm[col];
+          vc[m] = kx / x * sEcm[col];
+          vv[m] = to_f32(sV[j][col]);
+        }
+        kg[p] = make_split<P>(vg);
+        vf[p] = make_frag<P>(vv);
+        *reinterpret_cast<Frag*>(rec + R::KC + ((size_t)(it * 2 + p) * 64 + l) * sizeof(Frag)) = make_frag<P>(vc);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if (p > (rt >> 1)) break;   // T'[r][j] = 0 for j > r
+          mma_ss<P>(accW, kg[p], tf[rt][p]);
+          mma_sx<P>(accU, tf[rt][p], vf[p]);
+        }
+        Half hw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hw[e] = from_f32<In>(accW[e]);
+        In* wfrag = reinterpret_cast<In*>(rec + R::W) + ((size_t)(rt * KB + it / 2) * 64 + l) * 8;
+        *reinterpret_cast<Half*>(wfrag + 4 * (it & 1)) = hw;
+        *reinterpret_cast<f32x4*>(rec + R::U + ((size_t)(it * 4 + rt) * 64 + l) * 16) = accU;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: sequential pass over the chunks of one (sequence, head) for a
+// 16-column slice of S.  Wave w owns key rows [D/4 w, D/4 (w+1)) of the
+// slice as accumulators and token tile w of every chunk.
+// ---------------------------------------------------------------------------
+template <class P, int D>
+__global__ __launch_bounds__(kThreads) void prefill_state_kernel(
+    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin,
+    typename P::In* __restrict__ o, const unsigned char* __restrict__ ws) {
+  using In = typename P::In;
+  using Frag = typename P::Frag;
+  using Half = typename P::Half;
+  using R = Rec<P, D>;
+  constexpr int NV = D / 16, KB = D / 32, KTW = D / 64;
+
+  // XCD-aware order: the NV slices of one (sequence, head) share an XCD (and
+  // its L2) because workgroups are dealt to the 8 XCDs round-robin.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, rest = bid >> 3;
+  const int vt = rest % NV;
+  const int pair = (rest / NV) * 8 + xcd;
+  if (pair >= N * H) return;
+  const int n = pair / H, h = pair % H;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
+  const int col = 16 * vt + l16;
+  const int64_t bos = cu[n], eos = cu[n + 1];
+  const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
+  const int64_t slot0 = bos / kChunk + n;
+
+  __shared__ Frag sS[KB][64];
+  __shared__ Frag sE[2][2][64];   // [hi/lo][token block][lane]
+
+  const int64_t sbase = ((int64_t)n * H + h) * D;   // row (value channel) base of state[n][h]
+  f32x4 S[KTW];
+#pragma unroll
+  for (int kt = 0; kt < KTW; ++kt) {
+    const int kti = w * KTW + kt;
+    S[kt] = init ? *reinterpret_cast<const f32x4*>(init + (sbase + col) * D + 16 * kti + 4 * g)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int c = 0; c < nch; ++c) {
+    const unsigned char* rec = ws + ((size_t)(slot0 + c) * H + h) * R::BYTES;
+    const int64_t t0 = bos + (int64_t)c * kChunk;
+    const int len = (int)min<int64_t>(kChunk, eos - t0);
+
+    // S as the B operand (reduction over keys), rounded to the operand type
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int kti = w * KTW + kt;
+      Half hs;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hs[e] = from_f32<In>(S[kt][e]);
+      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[kti >> 1][l]) + 4 * (kti & 1)) = hs;
+    }
+    __syncthreads();
+
+    // token tile w: W S0 and Qg S0
+    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      const Frag sf = sS[p][l];
+      const Frag wf = *reinterpret_cast<const Frag*>(rec + R::W + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag));
+      const Frag qf = *reinterpret_cast<const Frag*>(rec + R::Q + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag));
+      mma(wsum, wf, sf);
+      mma(qsum, qf, sf);
+    }
+    // E = U - W S0 for token tile w, published split as the B operand of
+    // the reductions over tokens
+    const f32x4 u = *reinterpret_cast<const f32x4*>(rec + R::U + ((size_t)(vt * 4 + w) * 64 + l) * 16);
+    Half eh, el;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ev = u[e] - wsum[e];
+      eh[e] = from_f32<In>(ev);
+      el[e] = from_f32<In>(ev - to_f32(eh[e]));
+    }
+    *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[0][w >> 1][l]) + 4 * (w & 1)) = eh;
+    if constexpr (P::kSplit)
+      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[1][w >> 1][l]) + 4 * (w & 1)) = el;
+    __syncthreads();
+
+    // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int kti = w * KTW + kt;
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::G + (size_t)(16 * kti + 4 * g) * 4);
+      S[kt] *= gm;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const Frag kc = *reinterpret_cast<const Frag*>(rec + R::KC + ((size_t)(kti * 2 + p) * 64 + l) * sizeof(Frag));
+        mma(S[kt], kc, sE[0][p][l]);
+        if constexpr (P::kSplit) mma(S[kt], kc, sE[1][p][l]);
+      }
+    }
+    // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p > (w >> 1)) break;
+      const Frag bq = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)(w * 2 + p) * 64 + l) * sizeof(Frag));
+      mma(qsum, bq, sE[0][p][l]);
+      if constexpr (P::kSplit) mma(qsum, bq, sE[1][p][l]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * g + e;
+      if (r < len) o[((t0 + r) * H + h) * D + col] = from_f32<In>(qsum[e]);
+    }
+  }
+
+  if (fin) {
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int kti = w * KTW + kt;
+      *reinterpret_cast<f32x4*>(fin + (sbase + col) * D + 16 * kti + 4 * g) = S[kt];
+    }
+  }
+}
+
+template <class P, int D>
+static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
+  using In = typename P::In;
+  const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
+  if (A.total_tokens > 0) {
+    hipLaunchKernelGGL((prefill_prep_kernel<P, D>), dim3((unsigned)slots, (unsigned)A.num_heads),
+                       dim3(kThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
+                       A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads,
+                       (unsigned char*)A.workspace);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
+  const int64_t groups = (pairs + 7) / 8;
+  const unsigned blocks = (unsigned)(groups * 8 * (D / 16));
+  hipLaunchKernelGGL((prefill_state_kernel<P, D>), dim3(blocks), dim3(kThreads), 0, stream,
+                     A.cu_seqlens, A.num_seqs, A.num_heads, A.init_state, A.final_state,
+                     (In*)A.o, (const unsigned char*)A.workspace);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& A, hipStream_t stream) {
+  if (A.num_seqs == 0) return hipSuccess;
+  if (A.bf16) return A.d == 128 ? launch_prefill_t<PathBF16, 128>(A, stream)
+                                : launch_prefill_t<PathBF16, 64>(A, stream);
+  return A.d == 128 ? launch_prefill_t<PathF32, 128>(A, stream)
+                    : launch_prefill_t<PathF32, 64>(A, stream);
+}
+
+}  // namespace kda

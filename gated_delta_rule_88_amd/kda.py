@@ -1,0 +1,163 @@
+"""Python binding of the C ABI in include/kda.h (argument marshalling only).
+
+Every step of the operator runs in the HIP kernels of ``libkda.so``; this
+module checks that tensors live on the GPU with the layout the ABI states,
+passes their device pointers and torch's current HIP stream, and raises if
+the library reports an error.  There is no fallback path: if ``libkda.so``
+is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_DTYPE", 7: "KDA_ERR_HIP"}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load(path: str = LIB_PATH):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m gated_delta_rule_88_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_version.argtypes = []
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill_varlen.restype = ctypes.c_int
+    lib.kda_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                    ctypes.c_int, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def version() -> int:
+    return load().kda_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v/beta must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                   dtype: torch.dtype) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
+                       o=None, final_state=None, want_final: bool = True, workspace=None):
+    """Chunked prefill over packed sequences; returns ``(o, final_state)``.
+
+    q, k ``[T,H,dk]``; v ``[T,H,dv]`` (bf16 or fp32, one dtype); log_alpha
+    ``[T,H,dk]`` fp32; beta ``[T,H]``; cu_seqlens ``[N+1]`` int32 on the GPU;
+    init_state ``[N,H,dv,dk]`` fp32 or None.  ``final_state`` may be passed
+    (and may be ``init_state`` itself for an in-place continuation).
+    """
+    lib = load()
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", (T, H, dk), dt)
+    _check(k, "k", (T, H, dk), dt)
+    _check(v, "v", (T, H, dv), dt)
+    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32)
+    _check(beta, "beta", (T, H), dt)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, dv, dk), torch.float32)
+    if o is None:
+        o = torch.empty((T, H, dv), device=q.device, dtype=dt)
+    _check(o, "o", (T, H, dv), dt)
+    if final_state is None and want_final:
+        final_state = torch.empty((N, H, dv, dk), device=q.device, dtype=torch.float32)
+    if final_state is not None:
+        _check(final_state, "final_state", (N, H, dv, dk), torch.float32)
+    need = int(lib.kda_prefill_workspace_size(N, T, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(cu_seqlens), _ptr(init_state), _ptr(o), _ptr(final_state),
+                                N, T, H, dk, dv, code, _ptr(workspace), workspace.numel(),
+                                _stream(q.device))
+    if st != 0:
+        raise KdaError(st, "kda_prefill_varlen")
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
+    """One recurrent step; ``state [N,H,dv,dk]`` fp32 is updated in place.
+    Returns ``o [N,H,dv]``."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (N, H, dk), dt)
+    _check(k, "k", (N, H, dk), dt)
+    _check(v, "v", (N, H, dv), dt)
+    _check(log_alpha, "log_alpha", (N, H, dk), torch.float32)
+    _check(beta, "beta", (N, H), dt)
+    _check(state, "state", (N, H, dv, dk), torch.float32)
+    if o is None:
+        o = torch.empty((N, H, dv), device=q.device, dtype=dt)
+    _check(o, "o", (N, H, dv), dt)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(q.device))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return o

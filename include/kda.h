@@ -1,0 +1,150 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * The operator is the channel-wise gated delta rule of the page
+ * "Kimi Delta Attention" (architecture deep dive), §03 "KDA's specific
+ * innovation":
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (§02, read after the update)
+ *
+ * with S a dk x dv matrix per (sequence, head).  §06 "From recurrence to GPU
+ * kernels" names its two execution modes, which are the two entry points:
+ * a chunk-parallel prefill over blocks of tokens that carries only the final
+ * state across blocks (kda_prefill_varlen), and a fused recurrent step that
+ * consumes one q/k/v and gate set and updates the state in place
+ * (kda_decode_step).  §07 "Prefix caching and state transport" fixes the
+ * state interface: initial and final recurrent states in, and out of, the
+ * prefill, so a prefix state can be restored and continued.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers to contiguous, row-major
+ *   buffers, 16-byte aligned, owned by the caller.  The library allocates
+ *   nothing, copies nothing between host and device, never synchronises and
+ *   keeps no global mutable state; it only enqueues kernels on `stream`
+ *   (0 = the null stream).  Buffers must stay valid until that work is done.
+ * - log_alpha is the natural logarithm of the decay gate alpha (fp32, <= 0):
+ *   alpha_t[i] in (0, 1) decays key channel i (the per-channel gate of the
+ *   "Kimi Linear Guide" page, section "2. Channel-Wise Data-Dependent
+ *   Gating").  The GPU path supports log_alpha in [-2.5, 0]; values outside
+ *   give undefined (possibly non-finite) results and are not checked.
+ * - beta is one scalar write strength per token and head (§03).
+ * - q, k, v, beta and o share one element type `dtype`; the state is fp32.
+ * - State layout (init_state, final_state, decode state):
+ *       state[n][h][j][i] = S_{ij}      i = key channel, j = value channel
+ *   i.e. S^T row-major with the key index contiguous.  A prefill's final
+ *   state can be fed unchanged to the decode step or to a later prefill.
+ * - No query scaling is applied and q, k are used as given (the caller
+ *   normalises keys, as §02 assumes).
+ * - Validation happens on the host, before any HIP call, and returns a
+ *   status; no exception or abort crosses this interface.  The contents of
+ *   device arrays (cu_seqlens, gate values) are not inspected.
+ * - Supported: dk == dv in {64, 128}; dtype KDA_BF16 or KDA_F32.
+ * - Results are bitwise reproducible run to run on the same device (no
+ *   atomics, fixed reduction order).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  KDA_ERR_UNSUPPORTED = 3, /* head size not in {64, 128} or dk != dv */
+  KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  KDA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  KDA_ERR_DTYPE = 6,       /* unknown element type */
+  KDA_ERR_HIP = 7          /* a kernel launch failed */
+} kda_status;
+
+typedef enum kda_dtype {
+  KDA_BF16 = 0, /* bfloat16 q, k, v, beta and o; fp32 state and accumulation */
+  KDA_F32 = 1   /* float32 everywhere */
+} kda_dtype;
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+/*
+ * Bytes of device workspace kda_prefill_varlen needs for these sizes
+ * (0 on invalid sizes).  Depends only on the arguments.  The workspace holds
+ * per-chunk factors of the chunked form; its contents need not be
+ * initialised and are meaningless after the call.
+ */
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                  int32_t num_heads, int32_t dk, int32_t dv,
+                                  kda_dtype dtype);
+
+/*
+ * Chunk-parallel prefill over variable-length packed sequences
+ * ("Kimi Delta Attention" §06, chunk-parallel mode; chunks of 64 tokens as
+ * in the "Kimi Linear Guide" hardware-chunking section).  Sequence n
+ * occupies tokens [cu_seqlens[n], cu_seqlens[n+1]); chunks start at each
+ * sequence's first token and the last one may be partial.  Tokens of
+ * different sequences never interact.
+ *
+ *   q, k        [total_tokens, num_heads, dk]  dtype
+ *   v           [total_tokens, num_heads, dv]  dtype
+ *   log_alpha   [total_tokens, num_heads, dk]  fp32
+ *   beta        [total_tokens, num_heads]      dtype
+ *   cu_seqlens  [num_seqs + 1] int32 device array: cu[0] = 0,
+ *               non-decreasing, cu[num_seqs] = total_tokens (not checked)
+ *   init_state  [num_seqs, num_heads, dv, dk] fp32, or NULL for zero states
+ *   o           [total_tokens, num_heads, dv]  dtype (output)
+ *   final_state [num_seqs, num_heads, dv, dk] fp32 (output), or NULL to skip.
+ *               May equal init_state (in-place continuation); no other
+ *               aliasing between arguments is allowed.
+ *   workspace   device buffer of at least kda_prefill_workspace_size(...)
+ *               bytes (16-byte aligned)
+ *
+ * A sequence of length 0 produces no outputs and final_state = init_state
+ * (or zeros).  total_tokens may be 0.
+ */
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const void* beta,
+                              const int32_t* cu_seqlens,
+                              const float* init_state,
+                              void* o, float* final_state,
+                              int32_t num_seqs, int64_t total_tokens,
+                              int32_t num_heads, int32_t dk, int32_t dv,
+                              kda_dtype dtype,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * One recurrent decode step for num_seqs sequences x num_heads heads
+ * ("Kimi Delta Attention" §06, fused recurrent mode: decay, correct and
+ * write the state in place, then read the output).
+ *
+ *   q, k       [num_seqs, num_heads, dk]  dtype
+ *   v          [num_seqs, num_heads, dv]  dtype
+ *   log_alpha  [num_seqs, num_heads, dk]  fp32
+ *   beta       [num_seqs, num_heads]      dtype
+ *   state      [num_seqs, num_heads, dv, dk] fp32, read and overwritten
+ *   o          [num_seqs, num_heads, dv]  dtype (output)
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const void* beta,
+                           float* state, void* o,
+                           int32_t num_seqs, int32_t num_heads,
+                           int32_t dk, int32_t dv, kda_dtype dtype,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,110 @@
+"""Host-only checks of the C ABI: the library loads, exports what
+include/kda.h declares, sizes workspaces, and rejects bad arguments before
+any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_88_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH),
+                                reason="libkda.so not built (python -m gated_delta_rule_88_amd.build)")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, DTYPE = 0, 1, 2, 3, 4, 5, 6
+BF16, F32 = kda.KDA_BF16, kda.KDA_F32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(kda_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"kda_prefill_varlen", "kda_decode_step", "kda_prefill_workspace_size",
+                          "kda_status_string", "kda_version"}
+    for name in names:
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_status_strings_and_version(lib):
+    for s in range(0, 8):
+        assert kda.status_string(s)
+    assert kda.status_string(99) == "unknown status"
+    assert kda.version() >= 100
+
+
+def test_workspace_size(lib):
+    f = lib.kda_prefill_workspace_size
+    rec_bf16_128 = 4 * 4 * 1024 * 2 + 8 * 2 * 1024 + 8 * 1024 + 8 * 4 * 1024 + 128 * 4
+    assert f(1, 8192, 32, 128, 128, BF16) == (8192 // 64 + 1 + 1) * 32 * rec_bf16_128
+    assert f(1, 256, 1, 64, 64, F32) > 0
+    assert f(0, 0, 1, 128, 128, BF16) > 0            # one spare slot per head
+    assert f(1, 100, 2, 96, 96, BF16) == 0            # unsupported head size
+    assert f(1, 100, 2, 128, 64, BF16) == 0           # dk != dv
+    assert f(1, 100, 0, 128, 128, BF16) == 0
+    assert f(1, 100, 2, 128, 128, 7) == 0
+    assert f(1, -1, 2, 128, 128, BF16) == 0
+
+
+P = ctypes.c_void_p(0x10000)     # aligned fake device pointer (never dereferenced)
+MIS = ctypes.c_void_p(0x10008)   # 8-byte aligned only
+
+
+def prefill(lib, **over):
+    args = dict(q=P, k=P, v=P, la=P, beta=P, cu=P, init=None, o=P, fin=P, N=1, T=128, H=2,
+                dk=128, dv=128, dtype=BF16, ws=P, wsb=1 << 40, stream=None)
+    args.update(over)
+    return lib.kda_prefill_varlen(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                  args["cu"], args["init"], args["o"], args["fin"], args["N"],
+                                  args["T"], args["H"], args["dk"], args["dv"], args["dtype"],
+                                  args["ws"], args["wsb"], args["stream"])
+
+
+def decode(lib, **over):
+    args = dict(q=P, k=P, v=P, la=P, beta=P, state=P, o=P, N=4, H=2, dk=128, dv=128, dtype=BF16,
+                stream=None)
+    args.update(over)
+    return lib.kda_decode_step(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                               args["state"], args["o"], args["N"], args["H"], args["dk"],
+                               args["dv"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(la=None), NULL),
+    (dict(beta=None), NULL), (dict(cu=None), NULL), (dict(o=None), NULL),
+    (dict(N=0), SHAPE), (dict(N=-1), SHAPE), (dict(T=-5), SHAPE), (dict(H=0), SHAPE),
+    (dict(T=1 << 31), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(dk=128, dv=64), UNSUP), (dict(dk=256, dv=256), UNSUP),
+    (dict(dtype=5), DTYPE),
+    (dict(q=MIS), ALIGN), (dict(beta=MIS), ALIGN), (dict(init=MIS), ALIGN), (dict(ws=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=1024), WS),
+])
+def test_prefill_rejects(lib, over, expect):
+    assert prefill(lib, **over) == expect
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=None), NULL), (dict(state=None), NULL), (dict(o=None), NULL), (dict(beta=None), NULL),
+    (dict(N=-1), SHAPE), (dict(H=0), SHAPE), (dict(dk=32, dv=32), UNSUP), (dict(dk=64, dv=128), UNSUP),
+    (dict(dtype=2), DTYPE), (dict(state=MIS), ALIGN), (dict(la=MIS), ALIGN),
+])
+def test_decode_rejects(lib, over, expect):
+    assert decode(lib, **over) == expect
+
+
+def test_decode_zero_sequences_is_a_no_op(lib):
+    # nothing to launch: returns before touching HIP
+    assert decode(lib, N=0, q=None, state=None) == OK
