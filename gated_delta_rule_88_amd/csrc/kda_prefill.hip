@@ -38,19 +38,25 @@
 namespace kda {
 
 // ---------------------------------------------------------------------------
-// Per (chunk slot, head) record in the workspace.
+// Per (chunk slot, head) record in the workspace.  Operands whose rounding
+// to bf16 would show in the outputs are stored as a hi + lo pair (NS = 2):
+// Qg and S meet in the read-out Qg S0, where the result is often much
+// smaller than the terms; Kc feeds the state, which carries its error to
+// every later token; Bqk multiplies E in the intra-chunk read-out.  W enters
+// only through E and stays single.
 // ---------------------------------------------------------------------------
 template <class P, int D>
 struct Rec {
   static constexpr int ES = sizeof(typename P::In);
+  static constexpr int NS = P::kSplit ? 2 : 1;      // stored parts (hi, lo)
   static constexpr int KB = D / 32;                 // 32-deep key blocks
   static constexpr int NT = D / 16;                 // 16-wide key / value tiles
   static constexpr size_t FB = 64 * 8 * ES;         // bytes per fragment
-  static constexpr size_t W = 0;                    // [4 token tiles][KB]   W   (row token, k key)
-  static constexpr size_t Q = W + 4 * KB * FB;      // [4][KB]               Qg  (row token, k key)
-  static constexpr size_t KC = Q + 4 * KB * FB;     // [NT key tiles][2]     Kc^T (row key, k token)
-  static constexpr size_t B = KC + NT * 2 * FB;     // [4 token tiles][2]    Bqk (row token, k token)
-  static constexpr size_t U = B + 8 * FB;           // [NT value tiles][4 token tiles][64] f32x4
+  static constexpr size_t W = 0;                       // [4 token tiles][KB]       W    (row token, k key)
+  static constexpr size_t Q = W + 4 * KB * FB;         // [NS][4][KB]               Qg   (row token, k key)
+  static constexpr size_t KC = Q + NS * 4 * KB * FB;   // [NS][NT key tiles][2]     Kc^T (row key, k token)
+  static constexpr size_t B = KC + NS * NT * 2 * FB;   // [NS][4 token tiles][2]    Bqk  (row token, k token)
+  static constexpr size_t U = B + NS * 8 * FB;         // [NT value tiles][4 token tiles][64] f32x4
   static constexpr size_t G = U + (size_t)NT * 4 * 64 * 16;  // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
@@ -95,11 +101,22 @@ __device__ __forceinline__ f32x4 lds4(const __bf16* p) {
 }
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+
+template <class P>
+__device__ __forceinline__ void store_split(unsigned char* hi_base, unsigned char* lo_base, size_t off,
+                                            const Split<P>& s) {
+  using Frag = typename P::Frag;
+  *reinterpret_cast<Frag*>(hi_base + off) = s.hi;
+  if constexpr (P::kSplit) *reinterpret_cast<Frag*>(lo_base + off) = s.lo;
+}
+
 // ---------------------------------------------------------------------------
-// Kernel 1: per-chunk factors
+// Kernel 1: per-chunk factors.  512 threads (8 waves) per (chunk, head).
 // ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 512;
+
 template <class P, int D>
-__global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, const int32_t* __restrict__ cu, int N, int H,
@@ -109,19 +126,21 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
   using Half = typename P::Half;
   using R = Rec<P, D>;
   constexpr int C = kChunk;
-  constexpr int PI = D + 16 / (int)sizeof(In) * 1;  // row pitch of staged inputs (+16 bytes)
+  constexpr int NTH = kPrepThreads;
+  constexpr int NW = NTH / 64;                       // waves
+  constexpr int PI = D + 16 / (int)sizeof(In);       // row pitch of staged inputs (+16 bytes)
   constexpr int PX = D + 4;                          // row pitch of X
   constexpr int PL = C + 4;                          // row pitch of L and T
   constexpr int KB = D / 32, NT = D / 16;
+  constexpr size_t FS = sizeof(Frag);
   constexpr int QBYTES = (C * PI * (int)sizeof(In)) > (C * PL * 4) ? (C * PI * (int)sizeof(In)) : (C * PL * 4);
 
   __shared__ __align__(16) In sK[C][PI];
-  __shared__ __align__(16) In sV[C][PI];
   __shared__ __align__(16) unsigned char sQraw[QBYTES];   // Q, later T
-  __shared__ __align__(16) float sX[C][PX];               // e^(G - G[m])
+  __shared__ __align__(16) float sX[C][PX];               // X = e^(G - G[m])
   __shared__ __align__(16) float sL[C][PL];               // Diag(beta) A (strictly lower)
   __shared__ float sEgm[D], sEcm[D], sGm[D], sGc[D], sBeta[C];
-  __shared__ float sSeg[4][D];
+  __shared__ float sSeg[NTH / 64][D];
   __shared__ float sScr[4][16][17];
   In (*sQ)[PI] = reinterpret_cast<In (*)[PI]>(sQraw);
   float (*sT)[PL] = reinterpret_cast<float (*)[PL]>(sQraw);
@@ -136,30 +155,28 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
   const int w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
   unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
 
-  // ---- phase 1: stage K, Q, V rows, beta; clear L -------------------------
+  // ---- phase 1: stage K and Q rows, beta; clear L -------------------------
   {
     constexpr int EV = 16 / (int)sizeof(In);  // elements per 16-byte vector
     constexpr int VR = D / EV;                // vectors per row
-    for (int idx = tid; idx < C * VR; idx += kThreads) {
+    for (int idx = tid; idx < C * VR; idx += NTH) {
       const int r = idx / VR, cv = idx % VR;
-      uint4 kq = {0, 0, 0, 0}, qq = {0, 0, 0, 0}, vq = {0, 0, 0, 0};
+      uint4 kq = {0, 0, 0, 0}, qq = {0, 0, 0, 0};
       if (r < len) {
         const int64_t off = ((t0 + r) * H + h) * D + cv * EV;
         kq = *reinterpret_cast<const uint4*>(k + off);
         qq = *reinterpret_cast<const uint4*>(q + off);
-        vq = *reinterpret_cast<const uint4*>(v + off);
       }
       *reinterpret_cast<uint4*>(&sK[r][cv * EV]) = kq;
       *reinterpret_cast<uint4*>(&sQ[r][cv * EV]) = qq;
-      *reinterpret_cast<uint4*>(&sV[r][cv * EV]) = vq;
     }
     if (tid < C) sBeta[tid] = tid < len ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
-    for (int idx = tid; idx < C * PL; idx += kThreads) (&sL[0][0])[idx] = 0.f;
+    for (int idx = tid; idx < C * PL; idx += NTH) (&sL[0][0])[idx] = 0.f;
   }
 
   // ---- phase 2: cumulative log decay and the anchored factor X -------------
   {
-    constexpr int SEGS = kThreads / D;   // token segments per channel
+    constexpr int SEGS = NTH / D;        // token segments per channel
     constexpr int SL = C / SEGS;         // tokens per segment
     const int i = tid % D, s = tid / D;
     float gl[SL];
@@ -202,10 +219,10 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         const f32x4 a = lds4(&src[row][key]);
         const f32x4 x = *reinterpret_cast<const f32x4*>(&sX[row][key]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vals[4 * hh + e] = inv ? a[e] / x[e] : a[e] * x[e];
+        for (int e = 0; e < 4; ++e) vals[4 * hh + e] = inv ? a[e] * __builtin_amdgcn_rcpf(x[e]) : a[e] * x[e];
       }
     };
-    for (int pi = w; pi < 10; pi += 4) {
+    for (int pi = w; pi < 10; pi += NW) {
       // lower-triangular tile pairs (rt, jt), jt <= rt, in row order
       const int rt = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
       const int jt = pi - (rt * (rt + 1)) / 2;
@@ -225,42 +242,50 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         const int r = 16 * rt + 4 * g + e, j = 16 * jt + l16;
         sL[r][j] = (j < r) ? sBeta[r] * accA[e] : 0.f;
       }
-      // Bqk fragment (row tile rt, token block jt/2): lane l holds rows
-      // r = 16 rt + l16 and columns j = 16 jt + 4 g + e
-      Half hb;
+      // Bqk fragment (row tile rt, token block jt/2): lane l holds row
+      // r = 16 rt + l16 and columns j = 16 jt + 4 g + e, as hi and lo
+      Half hb, lb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 16 * jt + 4 * g + e, r = 16 * rt + l16;
-        hb[e] = from_f32<In>(j <= r ? accB[e] : 0.f);
+        const float x = j <= r ? accB[e] : 0.f;
+        hb[e] = from_f32<In>(x);
+        lb[e] = from_f32<In>(x - to_f32(hb[e]));
       }
-      In* bfrag = reinterpret_cast<In*>(rec + R::B) + ((size_t)(rt * 2 + jt / 2) * 64 + l) * 8;
-      *reinterpret_cast<Half*>(bfrag + 4 * (jt & 1)) = hb;
-      if (jt == rt && (rt & 1) == 0) {
+      const size_t foff = ((size_t)(rt * 2 + jt / 2) * 64 + l) * FS + 4 * (jt & 1) * sizeof(In);
+      *reinterpret_cast<Half*>(rec + R::B + foff) = hb;
+      if constexpr (P::kSplit) *reinterpret_cast<Half*>(rec + R::B + 8 * R::FB + foff) = lb;
+      if (jt == rt && (rt & 1) == 0) {   // columns above the diagonal block
         Half z;
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[e] = from_f32<In>(0.f);
-        *reinterpret_cast<Half*>(bfrag + 4) = z;   // columns above the diagonal
+        const size_t zoff = ((size_t)(rt * 2 + jt / 2) * 64 + l) * FS + 4 * sizeof(In);
+        *reinterpret_cast<Half*>(rec + R::B + zoff) = z;
+        if constexpr (P::kSplit) *reinterpret_cast<Half*>(rec + R::B + 8 * R::FB + zoff) = z;
       }
     }
-    // Qg fragments: token tile rt = w, all key blocks
-#pragma unroll
-    for (int p = 0; p < KB; ++p) {
+    // Qg fragments (token tile rt, key block p), hi and lo
+    for (int f = w; f < 4 * KB; f += NW) {
+      const int rt = f / KB, p = f % KB;
       float vq[8];
-      row_frag(sQ, 16 * w + l16, p, false, vq);
+      row_frag(sQ, 16 * rt + l16, p, false, vq);
 #pragma unroll
       for (int m = 0; m < 8; ++m) vq[m] *= sEgm[32 * p + kpos(g, m)];
-      *reinterpret_cast<Frag*>(rec + R::Q + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag)) = make_frag<P>(vq);
+      store_split<P>(rec + R::Q, rec + R::Q + 4 * KB * R::FB, ((size_t)f * 64 + l) * FS,
+                     make_split<P>(vq));
     }
   }
   __syncthreads();   // Q is dead from here on: its space becomes T
 
-  // ---- phase 4: T = (I + Diag(beta) A)^-1 by blocked forward substitution --
+  // ---- phase 4: T = (I + L)^-1, L = Diag(beta) A strictly lower ------------
+  // 16 x 16 diagonal blocks by forward substitution, then block doubling:
+  //   [[X, 0], [Y, Z]]^-1 = [[X^-1, 0], [-Z^-1 Y X^-1, Z^-1]]
+  // first for the 16-blocks (1,0) and (3,2), then for the 32-block (1,0).
   {
-    for (int idx = tid; idx < C * PL; idx += kThreads) (&sT[0][0])[idx] = 0.f;
+    for (int idx = tid; idx < C * PL; idx += NTH) (&sT[0][0])[idx] = 0.f;
     __syncthreads();
     if (w == 0) {
-      // the four 16 x 16 diagonal blocks: lane = (block, column)
-      const int bk = l >> 4, c = l & 15;
+      const int bk = l >> 4, c = l & 15;   // lane = (block, column)
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -273,43 +298,67 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
       for (int r = 0; r < 16; ++r) sT[16 * bk + r][16 * bk + c] = x[r];
     }
     __syncthreads();
-    // off-diagonal blocks, one column block per wave:
-    //   T_ba = -T_bb * sum_{kb=a}^{b-1} L_b,kb T_kb,a
-    const int a = w, c = l16, rr0 = 4 * g;
-    for (int step = 1; step < 4; ++step) {
-      const int bb = a + step;
-      const bool act = bb < 4;
-      if (act) {
-        float tmp[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = a; kb < bb; ++kb)
-          for (int qq = 0; qq < 16; ++qq) {
-            const float tv = sT[16 * kb + qq][16 * a + c];
+    const int c = l16, r0 = 4 * g;
+    // 16-block doubling: wave 0 -> block (1,0), wave 1 -> block (3,2)
+    if (w < 2) {
+      const int a = 2 * w, bb = a + 1;
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int qq = 0; qq < 16; ++qq) {
+        const float tv = sT[16 * a + qq][16 * a + c];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tmp[e] += sL[16 * bb + rr0 + e][16 * kb + qq] * tv;
-          }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sScr[w][rr0 + e][c] = tmp[e];
+        for (int e = 0; e < 4; ++e) x[e] += sL[16 * bb + r0 + e][16 * a + qq] * tv;
       }
-      __syncthreads();
-      if (act) {
-        float res[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int qq = 0; qq < 16; ++qq) {
-          const float tv = sScr[w][qq][c];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) res[e] -= sT[16 * bb + rr0 + e][16 * bb + qq] * tv;
+      for (int e = 0; e < 4; ++e) sScr[w][r0 + e][c] = x[e];
+    }
+    __syncthreads();
+    if (w < 2) {
+      const int a = 2 * w, bb = a + 1;
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int qq = 0; qq < 16; ++qq) {
+        const float tv = sScr[w][qq][c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] -= sT[16 * bb + r0 + e][16 * bb + qq] * tv;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[16 * bb + r0 + e][16 * a + c] = y[e];
+    }
+    __syncthreads();
+    // 32-block doubling: Y = L[32:64, 0:32] T[0:32, 0:32], then
+    // T[32:64, 0:32] = -T[32:64, 32:64] Y; wave w < 4 owns 16-tile (bi, bj)
+    if (w < 4) {
+      const int bi = w >> 1, bj = w & 1;
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = bj; kb < 2; ++kb)
+        for (int qq = 0; qq < 16; ++qq) {
+          const float tv = sT[16 * kb + qq][16 * bj + c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += sL[32 + 16 * bi + r0 + e][16 * kb + qq] * tv;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sT[16 * bb + rr0 + e][16 * a + c] = res[e];
-      }
-      __syncthreads();
+      for (int e = 0; e < 4; ++e) sScr[w][r0 + e][c] = y[e];
     }
+    __syncthreads();
+    if (w < 4) {
+      const int bi = w >> 1, bj = w & 1;
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb <= bi; ++kb)
+        for (int qq = 0; qq < 16; ++qq) {
+          const float tv = sScr[2 * kb + bj][qq][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] -= sT[32 + 16 * bi + r0 + e][32 + 16 * kb + qq] * tv;
+        }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[32 + 16 * bi + r0 + e][16 * bj + c] = z[e];
+    }
+    __syncthreads();
   }
 
   // ---- phase 5: W^T = Kg^T T'^T and U = T' V with T' = T Diag(beta);
   //               Kc^T fragments ---------------------------------------------
   {
-    // T' fragments (row tile rt, token block p); used as the B operand of
-    // W^T and the A operand of U (the two layouts coincide)
+    // T' fragments (row tile rt, token block p): the B operand of W^T and
+    // the A operand of U (the two layouts coincide)
     Split<P> tf[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -323,44 +372,62 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         }
         tf[rt][p] = make_split<P>(vals);
       }
-    constexpr int TPW = NT / 4;   // key (and value) tiles per wave
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const int it = w * TPW + tt;        // key tile for W and Kc, value tile for U
-      const int col = 16 * it + l16;
-      Split<P> kg[2];
-      Frag vf[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float vg[8], vc[8], vv[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int j = 32 * p + kpos(g, m);
-          const float kx = to_f32(sK[j][col]);
-          const float x = sX[j][col];
-          vg[m] = kx * x * sEgm[col];
-          vc[m] = kx / x * sEcm[col];
-          vv[m] = to_f32(sV[j][col]);
-        }
-        kg[p] = make_split<P>(vg);
-        vf[p] = make_frag<P>(vv);
-        *reinterpret_cast<Frag*>(rec + R::KC + ((size_t)(it * 2 + p) * 64 + l) * sizeof(Frag)) = make_frag<P>(vc);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f32x4 accW = {0.f, 0.f, 0.f, 0.f}, accU = {0.f, 0.f, 0.f, 0.f};
+    // tasks 0..NT-1: key tile (W, Kc); NT..2NT-1: value tile (U)
+    for (int task = w; task < 2 * NT; task += NW) {
+      if (task < NT) {
+        const int it = task;
+        const int col = 16 * it + l16;   // key channel of this lane
+        Split<P> kg[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          if (p > (rt >> 1)) break;   // T'[r][j] = 0 for j > r
-          mma_ss<P>(accW, kg[p], tf[rt][p]);
-          mma_sx<P>(accU, tf[rt][p], vf[p]);
-        }
-        Half hw;
+          float vg[8], vc[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hw[e] = from_f32<In>(accW[e]);
-        In* wfrag = reinterpret_cast<In*>(rec + R::W) + ((size_t)(rt * KB + it / 2) * 64 + l) * 8;
-        *reinterpret_cast<Half*>(wfrag + 4 * (it & 1)) = hw;
-        *reinterpret_cast<f32x4*>(rec + R::U + ((size_t)(it * 4 + rt) * 64 + l) * 16) = accU;
+          for (int m = 0; m < 8; ++m) {
+            const int j = 32 * p + kpos(g, m);
+            const float kx = to_f32(sK[j][col]);
+            const float x = sX[j][col];
+            vg[m] = kx * x * sEgm[col];
+            vc[m] = kx * __builtin_amdgcn_rcpf(x) * sEcm[col];
+          }
+          kg[p] = make_split<P>(vg);
+          store_split<P>(rec + R::KC, rec + R::KC + NT * 2 * R::FB,
+                         ((size_t)(it * 2 + p) * 64 + l) * FS, make_split<P>(vc));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 accW = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (p > (rt >> 1)) break;   // T'[r][j] = 0 for j > r
+            mma_ss<P>(accW, kg[p], tf[rt][p]);
+          }
+          Half hw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hw[e] = from_f32<In>(accW[e]);
+          const size_t off = ((size_t)(rt * KB + it / 2) * 64 + l) * FS + 4 * (it & 1) * sizeof(In);
+          *reinterpret_cast<Half*>(rec + R::W + off) = hw;
+        }
+      } else {
+        const int ct = task - NT;
+        const int col = 16 * ct + l16;   // value channel of this lane
+        Frag vf[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int j = 32 * p + kpos(g, m);
+            vf[p][m] = j < len ? v[((t0 + j) * H + h) * D + col] : from_f32<In>(0.f);
+          }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f32x4 accU = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (p > (rt >> 1)) break;
+            mma_sx<P>(accU, tf[rt][p], vf[p]);
+          }
+          *reinterpret_cast<f32x4*>(rec + R::U + ((size_t)(ct * 4 + rt) * 64 + l) * 16) = accU;
+        }
       }
     }
   }
@@ -369,8 +436,58 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 // ---------------------------------------------------------------------------
 // Kernel 2: sequential pass over the chunks of one (sequence, head) for a
 // 16-column slice of S.  Wave w owns key rows [D/4 w, D/4 (w+1)) of the
-// slice as accumulators and token tile w of every chunk.
+// slice as accumulators and token tile w of every chunk.  The operands of
+// chunk c+1 are loaded into registers while chunk c is computed.
 // ---------------------------------------------------------------------------
+template <class P, int D>
+struct ChunkOps {
+  using Frag = typename P::Frag;
+  static constexpr int KB = D / 32, KTW = D / 64, NS = P::kSplit ? 2 : 1;
+  Frag w[KB];          // W, token tile of this wave
+  Frag q[NS][KB];      // Qg hi/lo
+  Frag kc[NS][KTW][2]; // Kc^T hi/lo, key tiles of this wave
+  Frag b[NS][2];       // Bqk hi/lo
+  f32x4 u;             // U, token tile of this wave, this value slice
+  f32x4 gam[KTW];      // e^G[C-1] for this lane's key rows
+};
+
+template <class P, int D>
+__device__ __forceinline__ void load_ops(ChunkOps<P, D>& o, const unsigned char* __restrict__ rec,
+                                         int w, int l, int g, int vt) {
+  using Frag = typename P::Frag;
+  using R = Rec<P, D>;
+  using O = ChunkOps<P, D>;
+  constexpr size_t FS = sizeof(Frag);
+#pragma unroll
+  for (int p = 0; p < O::KB; ++p)
+    o.w[p] = *reinterpret_cast<const Frag*>(rec + R::W + ((size_t)(w * O::KB + p) * 64 + l) * FS);
+#pragma unroll
+  for (int s = 0; s < O::NS; ++s)
+#pragma unroll
+    for (int p = 0; p < O::KB; ++p)
+      o.q[s][p] = *reinterpret_cast<const Frag*>(rec + R::Q + ((size_t)((s * 4 + w) * O::KB + p) * 64 + l) * FS);
+#pragma unroll
+  for (int s = 0; s < O::NS; ++s)
+#pragma unroll
+    for (int kt = 0; kt < O::KTW; ++kt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int kti = w * O::KTW + kt;
+        o.kc[s][kt][p] = *reinterpret_cast<const Frag*>(
+            rec + R::KC + ((size_t)((s * R::NT + kti) * 2 + p) * 64 + l) * FS);
+      }
+#pragma unroll
+  for (int s = 0; s < O::NS; ++s)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      if (p <= (w >> 1))
+        o.b[s][p] = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)((s * 4 + w) * 2 + p) * 64 + l) * FS);
+  o.u = *reinterpret_cast<const f32x4*>(rec + R::U + ((size_t)(vt * 4 + w) * 64 + l) * 16);
+#pragma unroll
+  for (int kt = 0; kt < O::KTW; ++kt)
+    o.gam[kt] = *reinterpret_cast<const f32x4*>(rec + R::G + (size_t)(16 * (w * O::KTW + kt) + 4 * g) * 4);
+}
+
 template <class P, int D>
 __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin,
@@ -380,6 +497,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   using Half = typename P::Half;
   using R = Rec<P, D>;
   constexpr int NV = D / 16, KB = D / 32, KTW = D / 64;
+  constexpr int NS = P::kSplit ? 2 : 1;
 
   // XCD-aware order: the NV slices of one (sequence, head) share an XCD (and
   // its L2) because workgroups are dealt to the 8 XCDs round-robin.
@@ -397,8 +515,8 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = bos / kChunk + n;
 
-  __shared__ Frag sS[KB][64];
-  __shared__ Frag sE[2][2][64];   // [hi/lo][token block][lane]
+  __shared__ Frag sS[NS][KB][64];   // S as the B operand, hi/lo
+  __shared__ Frag sE[NS][2][64];    // E as the B operand, hi/lo
 
   const int64_t sbase = ((int64_t)n * H + h) * D;   // row (value channel) base of state[n][h]
   f32x4 S[KTW];
@@ -409,39 +527,50 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                  : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + c) * H + h) * R::BYTES; };
+  ChunkOps<P, D> cur, nxt;
+  if (nch > 0) load_ops<P, D>(cur, rec_of(0), w, l, g, vt);
+
   for (int c = 0; c < nch; ++c) {
-    const unsigned char* rec = ws + ((size_t)(slot0 + c) * H + h) * R::BYTES;
+    if (c + 1 < nch) load_ops<P, D>(nxt, rec_of(c + 1), w, l, g, vt);
     const int64_t t0 = bos + (int64_t)c * kChunk;
     const int len = (int)min<int64_t>(kChunk, eos - t0);
 
-    // S as the B operand (reduction over keys), rounded to the operand type
+    // S as the B operand (reduction over keys), hi and lo
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int kti = w * KTW + kt;
-      Half hs;
+      Half hs, ls;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hs[e] = from_f32<In>(S[kt][e]);
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[kti >> 1][l]) + 4 * (kti & 1)) = hs;
+      for (int e = 0; e < 4; ++e) {
+        hs[e] = from_f32<In>(S[kt][e]);
+        ls[e] = from_f32<In>(S[kt][e] - to_f32(hs[e]));
+      }
+      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[0][kti >> 1][l]) + 4 * (kti & 1)) = hs;
+      if constexpr (P::kSplit)
+        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[1][kti >> 1][l]) + 4 * (kti & 1)) = ls;
     }
     __syncthreads();
 
-    // token tile w: W S0 and Qg S0
+    // token tile w: W S0 (hi only: it only enters through E) and Qg S0 (split)
     f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
-      const Frag sf = sS[p][l];
-      const Frag wf = *reinterpret_cast<const Frag*>(rec + R::W + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag));
-      const Frag qf = *reinterpret_cast<const Frag*>(rec + R::Q + ((size_t)(w * KB + p) * 64 + l) * sizeof(Frag));
-      mma(wsum, wf, sf);
-      mma(qsum, qf, sf);
+      const Frag sh = sS[0][p][l];
+      mma(wsum, cur.w[p], sh);
+      mma(qsum, cur.q[0][p], sh);
+      if constexpr (P::kSplit) {
+        const Frag sl = sS[1][p][l];
+        mma(qsum, cur.q[0][p], sl);
+        mma(qsum, cur.q[1][p], sh);
+      }
     }
     // E = U - W S0 for token tile w, published split as the B operand of
     // the reductions over tokens
-    const f32x4 u = *reinterpret_cast<const f32x4*>(rec + R::U + ((size_t)(vt * 4 + w) * 64 + l) * 16);
     Half eh, el;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ev = u[e] - wsum[e];
+      const float ev = cur.u[e] - wsum[e];
       eh[e] = from_f32<In>(ev);
       el[e] = from_f32<In>(ev - to_f32(eh[e]));
     }
@@ -453,29 +582,34 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
-      const int kti = w * KTW + kt;
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::G + (size_t)(16 * kti + 4 * g) * 4);
-      S[kt] *= gm;
+      S[kt] *= cur.gam[kt];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const Frag kc = *reinterpret_cast<const Frag*>(rec + R::KC + ((size_t)(kti * 2 + p) * 64 + l) * sizeof(Frag));
-        mma(S[kt], kc, sE[0][p][l]);
-        if constexpr (P::kSplit) mma(S[kt], kc, sE[1][p][l]);
+        const Frag eh2 = sE[0][p][l];
+        mma(S[kt], cur.kc[0][kt][p], eh2);
+        if constexpr (P::kSplit) {
+          mma(S[kt], cur.kc[0][kt][p], sE[1][p][l]);
+          mma(S[kt], cur.kc[1][kt][p], eh2);
+        }
       }
     }
     // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (p > (w >> 1)) break;
-      const Frag bq = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)(w * 2 + p) * 64 + l) * sizeof(Frag));
-      mma(qsum, bq, sE[0][p][l]);
-      if constexpr (P::kSplit) mma(qsum, bq, sE[1][p][l]);
+      const Frag eh2 = sE[0][p][l];
+      mma(qsum, cur.b[0][p], eh2);
+      if constexpr (P::kSplit) {
+        mma(qsum, cur.b[0][p], sE[1][p][l]);
+        mma(qsum, cur.b[1][p], eh2);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + 4 * g + e;
       if (r < len) o[((t0 + r) * H + h) * D + col] = from_f32<In>(qsum[e]);
     }
+    cur = nxt;
   }
 
   if (fin) {
@@ -493,7 +627,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   if (A.total_tokens > 0) {
     hipLaunchKernelGGL((prefill_prep_kernel<P, D>), dim3((unsigned)slots, (unsigned)A.num_heads),
-                       dim3(kThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
+                       dim3(kPrepThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
                        A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads,
                        (unsigned char*)A.workspace);
     const hipError_t e = hipGetLastError();
