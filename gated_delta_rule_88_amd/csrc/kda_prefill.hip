@@ -476,12 +476,13 @@ __device__ __forceinline__ void load_ops(ChunkOps<P, D>& o, const unsigned char*
         o.kc[s][kt][p] = *reinterpret_cast<const Frag*>(
             rec + R::KC + ((size_t)((s * R::NT + kti) * 2 + p) * 64 + l) * FS);
       }
+  // both token blocks of Bqk are loaded (the second is unused for w < 2) so
+  // that every chunk issues the same loads and the waits stay exact
 #pragma unroll
   for (int s = 0; s < O::NS; ++s)
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      if (p <= (w >> 1))
-        o.b[s][p] = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)((s * 4 + w) * 2 + p) * 64 + l) * FS);
+      o.b[s][p] = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)((s * 4 + w) * 2 + p) * 64 + l) * FS);
   o.u = *reinterpret_cast<const f32x4*>(rec + R::U + ((size_t)(vt * 4 + w) * 64 + l) * 16);
 #pragma unroll
   for (int kt = 0; kt < O::KTW; ++kt)
@@ -527,89 +528,99 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                  : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + c) * H + h) * R::BYTES; };
-  ChunkOps<P, D> cur, nxt;
-  if (nch > 0) load_ops<P, D>(cur, rec_of(0), w, l, g, vt);
+  auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES; };
 
-  for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) load_ops<P, D>(nxt, rec_of(c + 1), w, l, g, vt);
-    const int64_t t0 = bos + (int64_t)c * kChunk;
-    const int len = (int)min<int64_t>(kChunk, eos - t0);
+  // one chunk step with operands `ops`
+  auto step = [&](const ChunkOps<P, D>& ops, int c) {
+      const int64_t t0 = bos + (int64_t)c * kChunk;
+      const int len = (int)min<int64_t>(kChunk, eos - t0);
 
-    // S as the B operand (reduction over keys), hi and lo
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      const int kti = w * KTW + kt;
-      Half hs, ls;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hs[e] = from_f32<In>(S[kt][e]);
-        ls[e] = from_f32<In>(S[kt][e] - to_f32(hs[e]));
+      // S as the B operand (reduction over keys), hi and lo
+  #pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        const int kti = w * KTW + kt;
+        Half hs, ls;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hs[e] = from_f32<In>(S[kt][e]);
+          ls[e] = from_f32<In>(S[kt][e] - to_f32(hs[e]));
+        }
+        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[0][kti >> 1][l]) + 4 * (kti & 1)) = hs;
+        if constexpr (P::kSplit)
+          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[1][kti >> 1][l]) + 4 * (kti & 1)) = ls;
       }
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[0][kti >> 1][l]) + 4 * (kti & 1)) = hs;
-      if constexpr (P::kSplit)
-        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[1][kti >> 1][l]) + 4 * (kti & 1)) = ls;
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // token tile w: W S0 (hi only: it only enters through E) and Qg S0 (split)
-    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < KB; ++p) {
-      const Frag sh = sS[0][p][l];
-      mma(wsum, cur.w[p], sh);
-      mma(qsum, cur.q[0][p], sh);
-      if constexpr (P::kSplit) {
-        const Frag sl = sS[1][p][l];
-        mma(qsum, cur.q[0][p], sl);
-        mma(qsum, cur.q[1][p], sh);
-      }
-    }
-    // E = U - W S0 for token tile w, published split as the B operand of
-    // the reductions over tokens
-    Half eh, el;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ev = cur.u[e] - wsum[e];
-      eh[e] = from_f32<In>(ev);
-      el[e] = from_f32<In>(ev - to_f32(eh[e]));
-    }
-    *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[0][w >> 1][l]) + 4 * (w & 1)) = eh;
-    if constexpr (P::kSplit)
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[1][w >> 1][l]) + 4 * (w & 1)) = el;
-    __syncthreads();
-
-    // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      S[kt] *= cur.gam[kt];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const Frag eh2 = sE[0][p][l];
-        mma(S[kt], cur.kc[0][kt][p], eh2);
+      // token tile w: W S0 (hi only: it only enters through E) and Qg S0 (split)
+      f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        const Frag sh = sS[0][p][l];
+        mma(wsum, ops.w[p], sh);
+        mma(qsum, ops.q[0][p], sh);
         if constexpr (P::kSplit) {
-          mma(S[kt], cur.kc[0][kt][p], sE[1][p][l]);
-          mma(S[kt], cur.kc[1][kt][p], eh2);
+          const Frag sl = sS[1][p][l];
+          mma(qsum, ops.q[0][p], sl);
+          mma(qsum, ops.q[1][p], sh);
         }
       }
-    }
-    // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if (p > (w >> 1)) break;
-      const Frag eh2 = sE[0][p][l];
-      mma(qsum, cur.b[0][p], eh2);
-      if constexpr (P::kSplit) {
-        mma(qsum, cur.b[0][p], sE[1][p][l]);
-        mma(qsum, cur.b[1][p], eh2);
+      // E = U - W S0 for token tile w, published split as the B operand of
+      // the reductions over tokens
+      Half eh, el;
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ev = ops.u[e] - wsum[e];
+        eh[e] = from_f32<In>(ev);
+        el[e] = from_f32<In>(ev - to_f32(eh[e]));
       }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * g + e;
-      if (r < len) o[((t0 + r) * H + h) * D + col] = from_f32<In>(qsum[e]);
-    }
-    cur = nxt;
+      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[0][w >> 1][l]) + 4 * (w & 1)) = eh;
+      if constexpr (P::kSplit)
+        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[1][w >> 1][l]) + 4 * (w & 1)) = el;
+      __syncthreads();
+
+      // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
+  #pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        S[kt] *= ops.gam[kt];
+  #pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const Frag eh2 = sE[0][p][l];
+          mma(S[kt], ops.kc[0][kt][p], eh2);
+          if constexpr (P::kSplit) {
+            mma(S[kt], ops.kc[0][kt][p], sE[1][p][l]);
+            mma(S[kt], ops.kc[1][kt][p], eh2);
+          }
+        }
+      }
+      // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
+  #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (p > (w >> 1)) break;
+        const Frag eh2 = sE[0][p][l];
+        mma(qsum, ops.b[0][p], eh2);
+        if constexpr (P::kSplit) {
+          mma(qsum, ops.b[0][p], sE[1][p][l]);
+          mma(qsum, ops.b[1][p], eh2);
+        }
+      }
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * g + e;
+        if (r < len) o[((t0 + r) * H + h) * D + col] = from_f32<In>(qsum[e]);
+      }
+  };
+
+  // ping-pong buffers: the loads for chunk c+1 are in flight while chunk c
+  // is computed; every iteration issues the same loads (past the last
+  // chunk the last record is read again), so the compiler's waits stay exact
+  ChunkOps<P, D> bufA, bufB;
+  if (nch > 0) load_ops<P, D>(bufA, rec_of(0), w, l, g, vt);
+  for (int c = 0; c < nch; c += 2) {
+    load_ops<P, D>(bufB, rec_of(c + 1), w, l, g, vt);
+    step(bufA, c);
+    if (c + 1 >= nch) break;
+    load_ops<P, D>(bufA, rec_of(c + 2), w, l, g, vt);
+    step(bufB, c + 1);
   }
 
   if (fin) {
