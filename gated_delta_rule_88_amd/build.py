@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_bf16.hip"]
 ARCH = "gfx950"
 
 

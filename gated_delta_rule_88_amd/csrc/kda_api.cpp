@@ -44,7 +44,8 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
   if (check_common(num_seqs, num_heads, dk, dv, dtype) != KDA_OK) return 0;
   if (total_tokens < 0 || total_tokens > INT32_MAX) return 0;
   const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
-  return (size_t)slots * (size_t)num_heads * kda::prefill_record_bytes(dk, dtype == KDA_BF16);
+  const size_t rec = dtype == KDA_BF16 ? kda::prefill_record_bytes_bf16(dk) : kda::prefill_record_bytes_f32(dk);
+  return (size_t)slots * (size_t)num_heads * rec;
 }
 
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
@@ -70,7 +71,8 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
   a.cu_seqlens = cu_seqlens; a.init_state = init_state; a.o = o; a.final_state = final_state;
   a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.num_heads = num_heads; a.d = dk;
   a.bf16 = dtype == KDA_BF16; a.workspace = workspace;
-  return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  const hipError_t e = a.bf16 ? kda::launch_prefill_bf16(a, stream) : kda::launch_prefill_f32(a, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

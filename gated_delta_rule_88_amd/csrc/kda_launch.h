@@ -33,12 +33,14 @@ struct PrefillArgs {
   void* workspace;
 };
 
-// Per-chunk factor record of the prefill (bytes), and the number of chunk
-// slots reserved for (num_seqs, total_tokens).
-size_t prefill_record_bytes(int d, bool bf16);
+// Per-chunk factor record of the prefill (bytes) for each precision path,
+// and the number of chunk slots reserved for (num_seqs, total_tokens).
+size_t prefill_record_bytes_f32(int d);
+size_t prefill_record_bytes_bf16(int d);
 int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kda

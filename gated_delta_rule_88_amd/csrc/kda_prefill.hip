@@ -1,4 +1,6 @@
-// kda_prefill.hip -- chunk-parallel KDA prefill over packed varlen sequences.
+// kda_prefill.hip -- chunk-parallel KDA prefill over packed varlen sequences,
+// fp32 inputs (the bf16 path is kda_prefill_bf16.hip; both share the chunk
+// equations and the slot map below).
 //
 // The recurrence (page "Kimi Delta Attention", §03)
 //     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t
@@ -34,6 +36,7 @@
 // in the recurrence, so the slices are independent.
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_prefill_common.h"
 
 namespace kda {
 
@@ -61,11 +64,6 @@ struct Rec {
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
 
-size_t prefill_record_bytes(int d, bool bf16) {
-  if (d == 128) return bf16 ? Rec<PathBF16, 128>::BYTES : Rec<PathF32, 128>::BYTES;
-  return bf16 ? Rec<PathBF16, 64>::BYTES : Rec<PathF32, 64>::BYTES;
-}
-
 // Chunk slots: chunk c of sequence n lives in slot cu[n]/64 + n + c.  Slots
 // of different sequences never collide (floor(a/64) + ceil(L/64) <=
 // floor((a+L)/64) + 1), and every slot is below T/64 + N + 1.
@@ -73,41 +71,8 @@ int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens) {
   return total_tokens / kChunk + num_seqs + 1;
 }
 
-__device__ __forceinline__ int64_t slot_key(const int32_t* cu, int n) {
-  return (int64_t)(cu[n] / kChunk) + n;
-}
-
-// slot -> (sequence, first token, length); false for an unused slot.
-__device__ __forceinline__ bool decode_slot(const int32_t* __restrict__ cu, int N, int64_t slot,
-                                            int& n, int64_t& t0, int& len) {
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (slot_key(cu, mid) <= slot) lo = mid; else hi = mid - 1;
-  }
-  n = lo;
-  const int64_t c = slot - slot_key(cu, lo);
-  const int64_t L = (int64_t)cu[lo + 1] - cu[lo];
-  if (c < 0 || c * kChunk >= L) return false;
-  t0 = cu[lo] + c * kChunk;
-  len = (int)min<int64_t>(kChunk, L - c * kChunk);
-  return true;
-}
-
-// four consecutive inputs of a token-major LDS row as fp32
-__device__ __forceinline__ f32x4 lds4(const __bf16* p) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-
-template <class P>
-__device__ __forceinline__ void store_split(unsigned char* hi_base, unsigned char* lo_base, size_t off,
-                                            const Split<P>& s) {
-  using Frag = typename P::Frag;
-  *reinterpret_cast<Frag*>(hi_base + off) = s.hi;
-  if constexpr (P::kSplit) *reinterpret_cast<Frag*>(lo_base + off) = s.lo;
+size_t prefill_record_bytes_f32(int d) {
+  return d == 128 ? Rec<PathF32, 128>::BYTES : Rec<PathF32, 64>::BYTES;
 }
 
 // ---------------------------------------------------------------------------
@@ -653,10 +618,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& A, hipStream_t stream) {
+hipError_t launch_prefill_f32(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs == 0) return hipSuccess;
-  if (A.bf16) return A.d == 128 ? launch_prefill_t<PathBF16, 128>(A, stream)
-                                : launch_prefill_t<PathBF16, 64>(A, stream);
   return A.d == 128 ? launch_prefill_t<PathF32, 128>(A, stream)
                     : launch_prefill_t<PathF32, 64>(A, stream);
 }

@@ -1,0 +1,50 @@
+// kda_prefill_common.h -- pieces shared by the prefill kernels: the chunk
+// slot map of packed variable-length sequences and small LDS helpers.
+#pragma once
+
+#include "kda_device.h"
+
+namespace kda {
+
+// Chunk slots: chunk c of sequence n lives in slot cu[n]/64 + n + c.  Slots
+// of different sequences never collide (floor(a/64) + ceil(L/64) <=
+// floor((a+L)/64) + 1), and every slot is below T/64 + N + 1.
+
+__device__ __forceinline__ int64_t slot_key(const int32_t* cu, int n) {
+  return (int64_t)(cu[n] / kChunk) + n;
+}
+
+// slot -> (sequence, first token, length); false for an unused slot.
+__device__ __forceinline__ bool decode_slot(const int32_t* __restrict__ cu, int N, int64_t slot,
+                                            int& n, int64_t& t0, int& len) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_key(cu, mid) <= slot) lo = mid; else hi = mid - 1;
+  }
+  n = lo;
+  const int64_t c = slot - slot_key(cu, lo);
+  const int64_t L = (int64_t)cu[lo + 1] - cu[lo];
+  if (c < 0 || c * kChunk >= L) return false;
+  t0 = cu[lo] + c * kChunk;
+  len = (int)min<int64_t>(kChunk, L - c * kChunk);
+  return true;
+}
+
+// four consecutive inputs of a token-major LDS row as fp32
+__device__ __forceinline__ f32x4 lds4(const __bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+
+template <class P>
+__device__ __forceinline__ void store_split(unsigned char* hi_base, unsigned char* lo_base, size_t off,
+                                            const Split<P>& s) {
+  using Frag = typename P::Frag;
+  *reinterpret_cast<Frag*>(hi_base + off) = s.hi;
+  if constexpr (P::kSplit) *reinterpret_cast<Frag*>(lo_base + off) = s.lo;
+}
+
+}  // namespace kda
