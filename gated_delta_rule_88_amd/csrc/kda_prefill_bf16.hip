@@ -51,18 +51,18 @@ struct Rec {
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
 
-// Raw inputs of one item held in registers: K and Q rows as 16-byte
-// vectors (token-major), log_alpha and V for this thread's channel over a
-// run of SL tokens (channel-major), beta for one token.
+// Raw inputs of one item held in registers, token-major, as 16-byte vectors
+// (K, Q, V rows in bf16, log_alpha rows in fp32), and beta for one token.
 template <int D>
 struct Prefetch {
-  static constexpr int VR = D / 8;                      // 16-byte vectors per row
-  static constexpr int NVT = C * VR / kPrepThreads;     // vectors per thread and tensor
-  static constexpr int SEGS = kPrepThreads / D;         // token runs per channel
+  static constexpr int VR = D / 8;                      // bf16 vectors per row
+  static constexpr int NVT = C * VR / kPrepThreads;     // bf16 vectors per thread and tensor
+  static constexpr int VRA = D / 4;                     // fp32 vectors per row
+  static constexpr int NVA = C * VRA / kPrepThreads;    // fp32 vectors per thread
+  static constexpr int SEGS = kPrepThreads / D;         // token runs per channel (cumulative sum)
   static constexpr int SL = C / SEGS;                   // tokens per run
-  uint4 k[NVT], q[NVT];
-  float la[SL];
-  In v[SL];
+  uint4 k[NVT], q[NVT], v[NVT];
+  f32x4 la[NVA];
   float beta;
 };
 
@@ -72,26 +72,26 @@ __device__ __forceinline__ void prefetch(Prefetch<D>& f, const In* __restrict__ 
                                          const In* __restrict__ beta, int H, int h, int64_t t0, int len,
                                          int tid) {
   using F = Prefetch<D>;
+  const int64_t base = (t0 * H + h) * D;   // first element of the item's rows
+  const int pitch = H * D;                 // elements between consecutive tokens
 #pragma unroll
   for (int i = 0; i < F::NVT; ++i) {
     const int idx = tid + i * kPrepThreads;
     const int r = idx / F::VR, cv = idx % F::VR;
-    f.k[i] = uint4{0, 0, 0, 0};
-    f.q[i] = uint4{0, 0, 0, 0};
+    f.k[i] = f.q[i] = f.v[i] = uint4{0, 0, 0, 0};
     if (r < len) {
-      const int64_t off = ((t0 + r) * H + h) * D + cv * 8;
-      f.k[i] = *reinterpret_cast<const uint4*>(k + off);
-      f.q[i] = *reinterpret_cast<const uint4*>(q + off);
+      const int off = r * pitch + cv * 8;
+      f.k[i] = *reinterpret_cast<const uint4*>(k + base + off);
+      f.q[i] = *reinterpret_cast<const uint4*>(q + base + off);
+      f.v[i] = *reinterpret_cast<const uint4*>(v + base + off);
     }
   }
-  const int ch = tid % D, sg = tid / D;
 #pragma unroll
-  for (int r = 0; r < F::SL; ++r) {
-    const int tok = sg * F::SL + r;
-    const bool ok = tok < len;
-    const int64_t off = ((t0 + tok) * H + h) * D + ch;
-    f.la[r] = ok ? la[off] : 0.f;
-    f.v[r] = ok ? v[off] : (In)0.f;
+  for (int i = 0; i < F::NVA; ++i) {
+    const int idx = tid + i * kPrepThreads;
+    const int r = idx / F::VRA, cv = idx % F::VRA;
+    f.la[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r < len) f.la[i] = *reinterpret_cast<const f32x4*>(la + base + r * pitch + cv * 4);
   }
   f.beta = (tid < len) ? (float)beta[(t0 + tid) * H + h] : 0.f;
 }
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
   // L = Diag(beta) A (strictly lower), T and the T' fragments
   __shared__ __align__(16) unsigned char sBig[BIGBYTES];
   __shared__ __align__(16) Frag sKg[NT][2][64];           // Kg^T fragments (row key, k token)
-  __shared__ __align__(16) Frag sVf[NT][2][64];           // V fragments (col value, k token)
+  __shared__ __align__(16) In sV[C][PI];                  // V rows
   __shared__ __align__(16) float sLdT[4][16][20];         // diagonal 16-blocks of L, transposed
   __shared__ float sEgm[D], sEcm[D], sGm[D], sGc[D], sBeta[C];
   __shared__ float sSeg[SEGS][D];
@@ -161,33 +161,41 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     const int h = (int)(item % H);
     unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
 
-    // ---- P1: prefetched rows to LDS; running sums of log_alpha ------------
+    // ---- P1: prefetched rows to LDS (log_alpha into the X buffer, V into
+    //      its fragments); running sums of log_alpha -------------------------
 #pragma unroll
     for (int i = 0; i < F::NVT; ++i) {
       const int idx = tid + i * kPrepThreads;
       const int r = idx / F::VR, cv = idx % F::VR;
       *reinterpret_cast<uint4*>(&sK[r][cv * 8]) = pf.k[i];
       *reinterpret_cast<uint4*>(&sQ[r][cv * 8]) = pf.q[i];
+      *reinterpret_cast<uint4*>(&sV[r][cv * 8]) = pf.v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < F::NVA; ++i) {
+      const int idx = tid + i * kPrepThreads;
+      const int r = idx / F::VRA, cv = idx % F::VRA;
+      *reinterpret_cast<f32x4*>(&sX[r][cv * 4]) = pf.la[i];
     }
     if (tid < C) sBeta[tid] = pf.beta;
-    float gl[SL], vv[SL];
-    {
-      float run = 0.f;
-#pragma unroll
-      for (int r = 0; r < SL; ++r) {
-        run += pf.la[r];
-        gl[r] = run;
-        vv[r] = (float)pf.v[r];
-      }
-      sSeg[sg][ch] = run;
-    }
     int n2, len2;
     int64_t t02;
     const int64_t item2 = next_item(cu, N, H, item + gridDim.x, n_items, n2, t02, len2);
     __syncthreads();
 
-    // ---- P2: cumulative log decay; X; Kg^T, Kc^T and V fragments ----------
+    // ---- P2: cumulative log decay; X; Kg^T and Kc^T fragments --------------
     {
+      float gl[SL];
+      {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < SL; ++r) {
+          run += sX[sg * SL + r][ch];
+          gl[r] = run;
+        }
+        sSeg[sg][ch] = run;
+      }
+      __syncthreads();
       float off = 0.f;
       for (int s2 = 0; s2 < sg; ++s2) off += sSeg[s2][ch];
 #pragma unroll
@@ -202,16 +210,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
         sEcm[ch] = ecm;
         reinterpret_cast<float*>(rec + R::G)[ch] = __expf(gc);
       }
-      // this channel is key ch (for Kg, Kc) and value ch (for V): tile ch/16,
-      // fragment row ch%16.  Four consecutive tokens j0..j0+3 of a 32-token
-      // block sit at fragment positions 4*hh .. 4*hh+3 of lane row + 16*gp.
+      // this channel is key ch: key tile ch/16, fragment row ch%16.  Four
+      // consecutive tokens j0..j0+3 of a 32-token block sit at fragment
+      // positions 4*hh .. 4*hh+3 of lane row + 16*gp.
       const int tile = ch >> 4, rowl = ch & 15;
 #pragma unroll
       for (int r0 = 0; r0 < SL; r0 += 4) {
         const int j0 = sg * SL + r0;
         const int p = j0 >> 5, jj = j0 & 31, gp = (jj & 15) >> 2, hh = jj >> 4;
         const int lane = rowl + 16 * gp;
-        Half kg4, kch4, kcl4, v4;
+        Half kg4, kch4, kcl4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + e;
@@ -222,10 +230,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
           const float kc = kx * __builtin_amdgcn_rcpf(x) * ecm;
           kch4[e] = (In)kc;
           kcl4[e] = (In)(kc - (float)kch4[e]);
-          v4[e] = (In)vv[r0 + e];
         }
         *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sKg[tile][p][lane]) + 4 * hh) = kg4;
-        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sVf[tile][p][lane]) + 4 * hh) = v4;
         const int koff = ((tile * 2 + p) * 64 + lane) * 16 + 8 * hh;
         *reinterpret_cast<Half*>(rec + R::KC + koff) = kch4;
         *reinterpret_cast<Half*>(rec + R::KC + NT * 2 * FB + koff) = kcl4;
@@ -243,29 +249,33 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
       }
       // staging slots: 0..3 Ka, 4..7 Kbar hi, 8..11 Kbar lo, 12..15 Qa hi,
       // 16..19 Qa lo; key block p+1 is built while block p is multiplied
+      // wave w builds half hh = w / 4 (keys 16 hh .. 16 hh + 15 of the block)
+      // of Ka, Kbar and Qa for row tile w % 4, reading K, Q and X once
       auto build = [&](int p, int buf) {
-        for (int task = w; task < 12; task += NW) {
-          const int kind = task >> 2, rt = task & 3;
-          const int row = 16 * rt + l16;
-          float vals[8];
+        const int rt = w & 3, hh = w >> 2;
+        const int row = 16 * rt + l16, key = 32 * p + 16 * hh + 4 * g;
+        const f32x4 kv = lds4(&sK[row][key]), qv = lds4(&sQ[row][key]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sX[row][key]);
+        Half ka, kbh, kbl, qah, qal;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int key = 32 * p + 16 * hh + 4 * g;
-            const f32x4 a = lds4(kind == 2 ? &sQ[row][key] : &sK[row][key]);
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&sX[row][key]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              vals[4 * hh + e] = kind == 1 ? a[e] * __builtin_amdgcn_rcpf(x[e]) : a[e] * x[e];
-          }
-          if (kind == 0) {
-            sStage[buf][rt][l] = make_frag<PathBF16>(vals);
-          } else {
-            const SplitB sp = make_split<PathBF16>(vals);
-            const int base = kind == 1 ? 4 : 12;
-            sStage[buf][base + rt][l] = sp.hi;
-            sStage[buf][base + 4 + rt][l] = sp.lo;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float a = kv[e] * x[e];
+          const float kb = kv[e] * __builtin_amdgcn_rcpf(x[e]);
+          const float qa = qv[e] * x[e];
+          ka[e] = (In)a;
+          kbh[e] = (In)kb;
+          kbl[e] = (In)(kb - (float)kbh[e]);
+          qah[e] = (In)qa;
+          qal[e] = (In)(qa - (float)qah[e]);
         }
+        auto put = [&](int slot, const Half& hv) {
+          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sStage[buf][slot][l]) + 4 * hh) = hv;
+        };
+        put(rt, ka);
+        put(4 + rt, kbh);
+        put(8 + rt, kbl);
+        put(12 + rt, qah);
+        put(16 + rt, qal);
       };
       build(0, 0);
       __syncthreads();
@@ -328,6 +338,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     // instruction s taken as 4 g + s, so that a row of the left factor is
     // one 16-byte LDS read and the right factor is an accumulator tile.
     {
+      // the next item's inputs are in flight from here on (most waves are
+      // idle in this phase)
+      if (item2 < n_items) prefetch<D>(pf, q, k, v, log_alpha, beta, H, (int)(item2 % H), t02, len2, tid);
       for (int idx = tid; idx < C * PL; idx += kPrepThreads) (&sT[0][0])[idx] = 0.f;
       const int bk = l >> 4, cc = l & 15;   // wave 0: lane = (block, column)
       float x[16];
@@ -410,9 +423,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     }
 
     // ---- P5: W, Q' = Qg - Bqk W, U = T' V, Bqk U -------------------------------
-    // the next item's inputs are in flight while this phase runs (issued
-    // here rather than earlier so that they hold no registers in P3 and P4)
-    if (item2 < n_items) prefetch<D>(pf, q, k, v, log_alpha, beta, H, (int)(item2 % H), t02, len2, tid);
     for (int task = w; task < 2 * NT; task += NW) {
       if (task < NT) {
         const int it = task;   // key tile
@@ -469,6 +479,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
         }
       } else {
         const int ct = task - NT;   // value tile
+        Frag vf[2];                 // V fragments (col value, k token)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) vf[p][m] = sV[32 * p + kpos(g, m)][16 * ct + l16];
         f32x4 uc[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -476,7 +491,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             if (p > (rt >> 1)) break;
-            mma(uc[rt], sTf[rt][p][l], sVf[ct][p][l]);
+            mma(uc[rt], sTf[rt][p][l], vf[p]);
           }
           *reinterpret_cast<f32x4*>(rec + R::U + ((ct * 4 + rt) * 64 + l) * 16) = uc[rt];
         }
