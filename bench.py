@@ -1,24 +1,37 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = one chunked prefill of the 8K workload (B=1, H=32, T=8192,
-d=128, bf16 inputs, fp32 state; P0-P4) followed by one decode step of the
-decode workload (256 sequences x 32 heads, 128x128 fp32 states, bf16 token
-inputs; D1-D4).  Inputs are synthetic, seeded, and resident in HBM before
-timing starts.
+d=128, bf16 inputs, fp32 state; chunk map, decay, UT/WY factors, state pass,
+output) followed by one decode step of the decode workload (256 sequences x
+32 heads, 128x128 fp32 states, bf16 token inputs).  Inputs are synthetic,
+seeded, and resident in HBM before timing starts.
 
 Prints one JSON line:
   value        prefill tokens/s of the 8K workload (8192 tokens x 32 heads per
                call) from HIP events around each prefill call
   ms_per_step  wall time of one whole step (prefill + decode step)
   decode       decode state GB/s and tokens/s from HIP events around each step
-  roofline     the dominant call (largest share of the step) against its bound
+  roofline     the call with the larger share of the step, against its bound
   cpu_baseline the fp64 oracle on the host cores, same prefill workload
+
+Other modes:
+  --part prefill|decode|copy   run one leg only (for profiler runs); "copy"
+                               is a plain 1 GiB device copy used to calibrate
+                               the memory counters
+  --traffic [OUTDIR]           run the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+                               as child processes and write the traffic record
+                               to OUTDIR/traffic_record.json and to profiles/
+                               (this process touches no GPU)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -28,6 +41,18 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_prefill_8k_decode_256.json")
+COPY_BYTES = 1 << 30
+
+
+def source_digest() -> str:
+    """sha256 of the HIP sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_88_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def prefill_algorithmic(T, H, d, n_seqs, init, final):
@@ -45,35 +70,119 @@ def decode_algorithmic(N, H, d):
     return N * H * (2 * d * d * 4 + 4 * d * 2 + d * 4 + 2)
 
 
-def cpu_baseline(prefill_inputs, seconds_hint=""):
+def cpu_baseline(prefill_inputs):
     import oracle
-    import torch
     d = prefill_inputs
     host = {k: d[k].cpu() for k in ("q", "k", "v", "log_alpha", "beta")}
     cu = d["cu_seqlens"].cpu().long()
     threads = oracle.default_threads()
-    t = time.perf_counter()
-    oracle.prefill(host["q"], host["k"], host["v"], host["log_alpha"], host["beta"], cu, None,
-                   nthreads=threads, want_final=True)
-    dt = time.perf_counter() - t
     T = host["q"].shape[0]
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    # repeat the whole call until about 10 s of host time have passed
+    reps, t0 = 0, time.perf_counter()
+    while reps < 100 and (reps == 0 or time.perf_counter() - t0 < 10.0):
+        oracle.prefill(host["q"], host["k"], host["v"], host["log_alpha"], host["beta"], cu, None,
+                       nthreads=threads, want_final=True)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole 8K prefill workload (T={T}, H={host['q'].shape[1]}, "
-                      f"d={host['q'].shape[2]}), fp64 token recurrence, {dt:.2f} s wall"}
+                      f"d={host['q'].shape[2]}, final state), fp64 token recurrence, "
+                      f"{reps} calls, {dt:.3f} s each"}
 
 
+def stored_traffic():
+    """Per-call HBM bytes from the stored counter record, if it matches the
+    current sources; else None."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_digest():
+        return None
+    return rec
+
+
+# ---------------------------------------------------------------------------
+# --traffic: counter passes in child processes
+# ---------------------------------------------------------------------------
+# kernels read from each part's run
+PART_KERNELS = {"copy": {"copy": "copyBuffer"},
+                "prefill": {"prep": "prep_kernel", "state": "state_kernel"},
+                "decode": {"decode": "decode_step_kernel"}}
+
+
+def _counter_pass(counter, part, outdir):
+    name = f"{part}_{counter}"
+    cmd = ["rocprofv3", "--pmc", counter, "-d", outdir, "-o", name, "--output-format", "csv",
+           "--", sys.executable, os.path.join(ROOT, "bench.py"), "--part", part,
+           "--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
+    env = dict(os.environ, TMPDIR="/tmp")
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(["timeout", "-s", "KILL", "120"] + cmd, check=True, cwd="/tmp", env=env)
+    rows = []
+    for path in glob.glob(os.path.join(outdir, "**", f"{name}_counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            rows += list(csv.DictReader(fh))
+    out = {}
+    for key, pat in PART_KERNELS[part].items():
+        vals = [float(r["Counter_Value"]) for r in rows if pat in r["Kernel_Name"]
+                and r["Counter_Name"] == counter]
+        if vals:
+            out[key] = sum(vals) / len(vals)   # KiB per dispatch
+    return out, " ".join(cmd)
+
+
+def run_traffic(outdir):
+    """Run the counter passes and write the traffic record."""
+    outdir = os.path.abspath(outdir)   # the passes run with /tmp as working directory
+    os.makedirs(outdir, exist_ok=True)
+    rec = {"source_sha": source_digest(), "unit": "KiB per dispatch", "commands": []}
+    for part in ("copy", "prefill", "decode"):
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals, cmd = _counter_pass(counter, part, outdir)
+            rec["commands"].append(cmd)
+            for k, v in vals.items():
+                rec.setdefault(k, {})[counter] = v
+    copy_kib = COPY_BYTES / 1024
+    rec["copy_factor_fetch"] = copy_kib / rec["copy"]["FETCH_SIZE"]
+    rec["copy_factor_write"] = copy_kib / rec["copy"]["WRITE_SIZE"]
+
+    def scaled(k):
+        c = rec[k]
+        return (c["FETCH_SIZE"] * rec["copy_factor_fetch"] + c["WRITE_SIZE"] * rec["copy_factor_write"]) * 1024
+
+    rec["prefill_call_bytes"] = scaled("prep") + scaled("state")
+    rec["prep_bytes"] = scaled("prep")
+    rec["state_bytes"] = scaled("state")
+    rec["decode_call_bytes"] = scaled("decode")
+    for path in (os.path.join(outdir, "traffic_record.json"), TRAFFIC_RECORD):
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+    print(json.dumps({k: rec[k] for k in ("prefill_call_bytes", "prep_bytes", "state_bytes",
+                                          "decode_call_bytes", "copy_factor_fetch",
+                                          "copy_factor_write")}), flush=True)
+
+
+# ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "copy"), default="all")
+    ap.add_argument("--traffic", metavar="OUTDIR", nargs="?", const=os.path.join(ROOT, "gpurun_out", "traffic"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              f"(the operator shards by (sequence, head) with no exchange; see DESIGN.md)",
+              f"(the operator shards by (sequence, head) with no exchange, see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.traffic:
+        run_traffic(args.traffic)
+        return
 
     import torch
     from gated_delta_rule_88_amd import inputs, kda
@@ -81,6 +190,15 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     kda.load()
+
+    if args.part == "copy":
+        src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+
     wl = inputs.WORKLOADS["prefill_8k"]
     P = inputs.prefill_inputs(wl, device=dev)
     T, H, D = P["q"].shape
@@ -102,6 +220,12 @@ def main():
         s %= n_dec
         kda.kda_decode_step(Dd["q"][s], Dd["k"][s], Dd["v"][s], Dd["log_alpha"][s], Dd["beta"][s],
                             state, o=od)
+
+    if args.part in ("prefill", "decode"):
+        for s in range(args.warmup + args.steps):
+            prefill() if args.part == "prefill" else decode(s)
+        torch.cuda.synchronize()
+        return
 
     for s in range(args.warmup):
         prefill()
@@ -130,14 +254,19 @@ def main():
     dbytes = decode_algorithmic(dwl.num_seqs, dwl.heads, dwl.dv)
     pre_gbps = pbytes / (pre_avg * 1e-3) / 1e9
     dec_gbps = dbytes / (dec_avg * 1e-3) / 1e9
+    traffic = stored_traffic()
     roof_pre = {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "call": "kda_prefill_varlen (prep + state-pass kernels)",
+                "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": round(traffic["prefill_call_bytes"]) if traffic else None,
+                "algorithmic_bytes": pbytes,
+                "launch": "kda_prefill_varlen: prep_kernel then state_kernel (one call)",
                 "mfma_tflops": round(pflops / (pre_avg * 1e-3) / 1e12, 2),
                 "mfma_frac": round(pflops / (pre_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "call": "kda_decode_step (decode_step_kernel)"}
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": round(traffic["decode_call_bytes"]) if traffic else None,
+                "algorithmic_bytes": dbytes,
+                "launch": "kda_decode_step: decode_step_kernel"}
     dominant = roof_dec if dec_avg > pre_avg else roof_pre
 
     out = {
@@ -157,7 +286,8 @@ def main():
                    "prefill": {"B": 1, "H": H, "T": T, "dk": D, "dv": D, "chunk": 64,
                                "init_state": None, "final_state": True},
                    "decode": {"sequences": dwl.num_seqs, "H": dwl.heads, "dk": dwl.dk,
-                              "dv": dwl.dv, "state_MB": round(dwl.num_seqs * dwl.heads * dwl.dk * dwl.dv * 4 / 1e6, 1)}},
+                              "dv": dwl.dv,
+                              "state_MB": round(dwl.num_seqs * dwl.heads * dwl.dk * dwl.dv * 4 / 1e6, 1)}},
         "prefill": {"ms": round(pre_avg, 5), "ms_min": round(min(pre_ms), 5),
                     "tokens_per_s": round(T / (pre_avg * 1e-3), 1), "roofline": roof_pre},
         "decode": {"ms": round(dec_avg, 5), "ms_min": round(min(dec_ms), 5),

@@ -13,19 +13,22 @@
 //   o_j   = r_j + (k . q) e_j               = (S_new^T q)_j
 //
 // Memory plan (HBM-bound: 2 x 64 KiB of state per head against 1.5 KiB of
-// token data): one workgroup of 256 threads per (sequence, head).  Sixteen
+// token data): one workgroup of 1024 threads per (sequence, head).  Sixteen
 // lanes own one state row at a time, each lane D/16 keys as float4 pieces,
 // so every load and store instruction of a wave moves four contiguous
 // 256-byte row segments.  A thread issues all of its row loads before any
-// arithmetic (16 float4 in flight per lane at D = 128).  The two dot
+// arithmetic.  The state is streamed with nontemporal loads and stores (it
+// is touched once per step and is larger than the caches).  The two dot
 // products reduce over the 16 lanes of a DPP row; no LDS and no barrier.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
+constexpr int kDecodeThreads = 1024;
+
 template <class P, int D>
-__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, float* __restrict__ state,
@@ -33,11 +36,11 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   using In = typename P::In;
   constexpr int NK = D / 16;        // keys per lane
   constexpr int NC = NK / 4;        // float4 pieces per lane and row
-  constexpr int ROWS = D / 16;      // rows per 16-lane group
+  constexpr int ROWS = D / (kDecodeThreads / 16);   // rows per 16-lane group
 
   const int64_t tok = blockIdx.x;   // n * H + h
   const int tid = threadIdx.x;
-  const int grp = tid >> 4;         // 16 groups of 16 lanes
+  const int grp = tid >> 4;         // groups of 16 lanes
   const int l16 = tid & 15;
 
   // token vectors for this lane's keys: c * 64 + 4 * l16 + {0..3}
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const int j = grp * ROWS + it;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      s[it][c] = *reinterpret_cast<const f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16);
+      s[it][c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16));
   }
 
   float my_o = 0.f;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
       f32x4 ns;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ns[e] = a[4 * c + e] * s[it][c][e] + kk[4 * c + e] * err;
-      *reinterpret_cast<f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16) = ns;
+      __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(srow0 + (int64_t)j * D + c * 64 + 4 * l16));
     }
   }
   if (l16 < ROWS) o[tok * D + grp * ROWS + l16] = from_f32<In>(my_o);
@@ -104,7 +107,7 @@ template <class P, int D>
 static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   using In = typename P::In;
   const unsigned blocks = (unsigned)((int64_t)A.num_seqs * A.num_heads);
-  hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
                      (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
                      (const In*)A.beta, A.state, (In*)A.o);
   return hipGetLastError();
