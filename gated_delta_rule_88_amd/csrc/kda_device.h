@@ -5,6 +5,7 @@
 // ---------------------------------------------------------
 // All matrix products run on the 16x16 output MFMA family:
 //   bf16:  v_mfma_f32_16x16x32_bf16  (one instruction per 32-deep block)
+//   fp16:  v_mfma_f32_16x16x32_f16   (one instruction per 32-deep block)
 //   fp32:  v_mfma_f32_16x16x4_f32    (eight instructions per 32-deep block)
 // For a 32-deep reduction block, lane l (g = l / 16, r = l % 16) holds the
 // row (A operand) or column (B operand) r of a 16-wide tile and eight
@@ -26,6 +27,8 @@ namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -60,6 +63,9 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 
 __device__ __forceinline__ void mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const f16x8& a, const f16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x4& acc, const f32x8& a, const f32x8& b) {
 #pragma unroll

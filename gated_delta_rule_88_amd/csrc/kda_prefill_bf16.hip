@@ -11,14 +11,16 @@
 // Kernel 1 (prep) is persistent: each workgroup walks (chunk, head) items
 // and loads the raw inputs of its next item into registers while it
 // computes the current one.  Per item it produces, as MFMA fragments:
-// W (bf16), Q' and Kc^T (bf16 hi + lo), U and Bqk U (fp32 accumulator
-// tiles) and e^G[C-1].
+// W, Q' and Kc^T (fp16), U and Bqk U (fp32 accumulator tiles) and e^G[C-1].
 //
-// Precision (bf16 operands, fp32 accumulation): an operand whose rounding
-// would show in the outputs is split into hi + lo bf16 parts and multiplied
-// as hi*hi + hi*lo + lo*hi: Q and K scaled by the decay in Q K^T (the
-// intra-chunk matrix Bqk), Bqk itself, Q', Kc, U in Bqk U, S in Q' S, and E
-// in the state update.  The K K^T operands, T, Kg and W stay single.
+// Precision (fp32 accumulation throughout).  Inside the prep, an operand
+// whose bf16 rounding would show in the outputs is split into hi + lo bf16
+// parts and multiplied as hi*hi + hi*lo + lo*hi: Q and K scaled by the decay
+// in Q K^T (the intra-chunk matrix Bqk), Bqk itself and U in Bqk U.  The
+// K K^T operands, T and Kg stay single bf16.  The decay-scaled operands
+// there span up to e^(+-80) (the anchor sits mid-chunk), which only bf16
+// covers.  The operands of the sequential pass -- W, Q', Kc, S and E -- are
+// all of moderate size and go through single fp16 (11-bit significand).
 //
 // Kernel 2 (state pass) is one workgroup per (sequence, head, 16 value
 // columns): S's columns never mix in the recurrence.  Per chunk:
@@ -33,6 +35,8 @@ namespace bf {
 using In = __bf16;
 using Frag = bf16x8;
 using Half = bf16x4;
+using HFrag = f16x8;    // fp16 operands of the sequential pass
+using HHalf = f16x4;
 using SplitB = Split<PathBF16>;
 constexpr int C = kChunk;
 constexpr size_t FB = 64 * sizeof(Frag);   // bytes per fragment
@@ -43,9 +47,9 @@ template <int D>
 struct Rec {
   static constexpr int KB = D / 32, NT = D / 16;
   static constexpr size_t W = 0;                             // [4 token tiles][KB]          W
-  static constexpr size_t QP = W + 4 * KB * FB;              // [hi,lo][4 token tiles][KB]   Q'
-  static constexpr size_t KC = QP + 2 * 4 * KB * FB;         // [hi,lo][NT key tiles][2]     Kc^T
-  static constexpr size_t U = KC + 2 * NT * 2 * FB;          // [NT value tiles][4 token tiles][64] f32x4
+  static constexpr size_t QP = W + 4 * KB * FB;              // [4 token tiles][KB]          Q'
+  static constexpr size_t KC = QP + 4 * KB * FB;             // [NT key tiles][2]            Kc^T
+  static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f32x4
   static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 16; // same layout, Bqk U
   static constexpr size_t G = BU + (size_t)NT * 4 * 64 * 16; // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
@@ -219,7 +223,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
         const int j0 = sg * SL + r0;
         const int p = j0 >> 5, jj = j0 & 31, gp = (jj & 15) >> 2, hh = jj >> 4;
         const int lane = rowl + 16 * gp;
-        Half kg4, kch4, kcl4;
+        Half kg4;
+        HHalf kc4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + e;
@@ -227,14 +232,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
           sX[j][ch] = x;
           const float kx = (float)sK[j][ch];
           kg4[e] = (In)(kx * x * egm);
-          const float kc = kx * __builtin_amdgcn_rcpf(x) * ecm;
-          kch4[e] = (In)kc;
-          kcl4[e] = (In)(kc - (float)kch4[e]);
+          kc4[e] = (_Float16)(kx * __builtin_amdgcn_rcpf(x) * ecm);
         }
         *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sKg[tile][p][lane]) + 4 * hh) = kg4;
         const int koff = ((tile * 2 + p) * 64 + lane) * 16 + 8 * hh;
-        *reinterpret_cast<Half*>(rec + R::KC + koff) = kch4;
-        *reinterpret_cast<Half*>(rec + R::KC + NT * 2 * FB + koff) = kcl4;
+        *reinterpret_cast<HHalf*>(rec + R::KC + koff) = kc4;
       }
     }
     __syncthreads();
@@ -438,10 +440,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
             mma(wc[rt], tf, kg);   // W[r][i]
             mma(wt, kg, tf);       // W^T[i][r]
           }
-          Half hw;
+          HHalf hw;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hw[e] = (In)wt[e];
-          *reinterpret_cast<Half*>(rec + R::W + ((rt * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hw;
+          for (int e = 0; e < 4; ++e) hw[e] = (_Float16)wt[e];
+          *reinterpret_cast<HHalf*>(rec + R::W + ((rt * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hw;
         }
         // -W^T as the A operand over token block p (from the W tiles 2p, 2p+1)
         Frag wn[2];
@@ -467,15 +469,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
             mma(acc, wn[p], sBq[0][rt][p][l]);
             mma(acc, wn[p], sBq[1][rt][p][l]);
           }
-          Half hq, lq;
+          HHalf hq;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hq[e] = (In)acc[e];
-            lq[e] = (In)(acc[e] - (float)hq[e]);
-          }
+          for (int e = 0; e < 4; ++e) hq[e] = (_Float16)acc[e];
           const int qo = ((rt * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1);
-          *reinterpret_cast<Half*>(rec + R::QP + qo) = hq;
-          *reinterpret_cast<Half*>(rec + R::QP + 4 * KB * FB + qo) = lq;
+          *reinterpret_cast<HHalf*>(rec + R::QP + qo) = hq;
         }
       } else {
         const int ct = task - NT;   // value tile
@@ -534,20 +532,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 // ---------------------------------------------------------------------------
 // Kernel 2: sequential pass over the chunks of one (sequence, head) for a
 // 16-column slice of S.  Wave w owns key rows [D/4 w, D/4 (w+1)) of the
-// slice as accumulators and token tile w of every chunk; the next chunk's
-// operands are in flight while the current one is computed.
+// slice as accumulators and token tile w of every chunk; the operands of
+// the next two chunks are in flight while the current one is computed.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Ops {
   static constexpr int KB = D / 32, KTW = D / 64;
-  Frag w[KB];            // W, token tile of this wave
-  Frag qp[2][KB];        // Q' hi, lo
-  Frag kc[2][KTW][2];    // Kc^T hi, lo for this wave's key tiles
+  HFrag w[KB];           // W, token tile of this wave
+  HFrag qp[KB];          // Q', token tile of this wave
+  HFrag kc[KTW][2];      // Kc^T for this wave's key tiles
   f32x4 u, bu;           // U and Bqk U, token tile of this wave, this slice
   f32x4 gam[KTW];        // e^G[C-1] for this lane's key rows
 };
 
-// The operand loads of one chunk, in four parts that the step spreads over
+// The operand loads of one chunk, in three parts that the step spreads over
 // its phases so that the vector memory path works while the MFMAs do.
 template <int D>
 __device__ __forceinline__ void load_ops_part(Ops<D>& o, const unsigned char* __restrict__ rec, int part, int w,
@@ -557,25 +555,21 @@ __device__ __forceinline__ void load_ops_part(Ops<D>& o, const unsigned char* __
   if (part == 0) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
-      o.w[p] = *reinterpret_cast<const Frag*>(rec + R::W + ((w * O::KB + p) * 64 + l) * 16);
+      o.w[p] = *reinterpret_cast<const HFrag*>(rec + R::W + ((w * O::KB + p) * 64 + l) * 16);
     o.u = *reinterpret_cast<const f32x4*>(rec + R::U + ((vt * 4 + w) * 64 + l) * 16);
     o.bu = *reinterpret_cast<const f32x4*>(rec + R::BU + ((vt * 4 + w) * 64 + l) * 16);
-  } else if (part == 1 || part == 2) {
-    const int s = part - 1;
+  } else if (part == 1) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
-      o.qp[s][p] = *reinterpret_cast<const Frag*>(rec + R::QP + (((s * 4 + w) * O::KB + p) * 64 + l) * 16);
+      o.qp[p] = *reinterpret_cast<const HFrag*>(rec + R::QP + ((w * O::KB + p) * 64 + l) * 16);
   } else {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int kt = 0; kt < O::KTW; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < O::KTW; ++kt)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int kti = w * O::KTW + kt;
-          o.kc[s][kt][p] =
-              *reinterpret_cast<const Frag*>(rec + R::KC + (((s * R::NT + kti) * 2 + p) * 64 + l) * 16);
-        }
+      for (int p = 0; p < 2; ++p) {
+        const int kti = w * O::KTW + kt;
+        o.kc[kt][p] = *reinterpret_cast<const HFrag*>(rec + R::KC + ((kti * 2 + p) * 64 + l) * 16);
+      }
 #pragma unroll
     for (int kt = 0; kt < O::KTW; ++kt)
       o.gam[kt] = *reinterpret_cast<const f32x4*>(rec + R::G + (16 * (w * O::KTW + kt) + 4 * g) * 4);
@@ -586,7 +580,7 @@ template <int D>
 __device__ __forceinline__ void load_ops(Ops<D>& o, const unsigned char* __restrict__ rec, int w, int l, int g,
                                          int vt) {
 #pragma unroll
-  for (int part = 0; part < 4; ++part) load_ops_part<D>(o, rec, part, w, l, g, vt);
+  for (int part = 0; part < 3; ++part) load_ops_part<D>(o, rec, part, w, l, g, vt);
 }
 
 template <int D>
@@ -612,8 +606,8 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
   const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = bos / kChunk + n;
 
-  __shared__ Frag sS[2][KB][64];   // S as the B operand, hi and lo
-  __shared__ Frag sE[2][2][64];    // E as the B operand, hi and lo
+  __shared__ HFrag sS[KB][64];   // S as the B operand
+  __shared__ HFrag sE[2][64];    // E as the B operand
 
   const int64_t sbase = ((int64_t)n * H + h) * D;
   f32x4 S[KTW];
@@ -635,38 +629,26 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int kti = w * KTW + kt;
-      Half hs, ls;
+      HHalf hs;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hs[e] = (In)S[kt][e];
-        ls[e] = (In)(S[kt][e] - (float)hs[e]);
-      }
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[0][kti >> 1][l]) + 4 * (kti & 1)) = hs;
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[1][kti >> 1][l]) + 4 * (kti & 1)) = ls;
+      for (int e = 0; e < 4; ++e) hs[e] = (_Float16)S[kt][e];
+      *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sS[kti >> 1][l]) + 4 * (kti & 1)) = hs;
     }
     __syncthreads();
     load_ops_part<D>(nxt, nrec, 1, w, l, g, vt);
-    // token tile w: W S (single) and Q' S (split)
+    // token tile w: W S and Q' S
     f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = ops.bu;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
-      const Frag sh = sS[0][p][l], sl = sS[1][p][l];
-      mma(wsum, ops.w[p], sh);
-      mma(qsum, ops.qp[0][p], sh);
-      mma(qsum, ops.qp[0][p], sl);
-      mma(qsum, ops.qp[1][p], sh);
+      const HFrag sf = sS[p][l];
+      mma(wsum, ops.w[p], sf);
+      mma(qsum, ops.qp[p], sf);
     }
-    load_ops_part<D>(nxt, nrec, 2, w, l, g, vt);
-    // E = U - W S, published split as the B operand over tokens
-    Half eh, el;
+    // E = U - W S, published as the B operand over tokens
+    HHalf eh;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ev = ops.u[e] - wsum[e];
-      eh[e] = (In)ev;
-      el[e] = (In)(ev - (float)eh[e]);
-    }
-    *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[0][w >> 1][l]) + 4 * (w & 1)) = eh;
-    *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[1][w >> 1][l]) + 4 * (w & 1)) = el;
+    for (int e = 0; e < 4; ++e) eh[e] = (_Float16)(ops.u[e] - wsum[e]);
+    *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[w >> 1][l]) + 4 * (w & 1)) = eh;
     // O = Q' S + Bqk U for token tile w
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -674,26 +656,20 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
       if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
     }
     __syncthreads();
-    load_ops_part<D>(nxt, nrec, 3, w, l, g, vt);
+    load_ops_part<D>(nxt, nrec, 2, w, l, g, vt);
     // S <- Diag(e^G[C-1]) S + Kc^T E
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       S[kt] *= ops.gam[kt];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const Frag e_h = sE[0][p][l], e_l = sE[1][p][l];
-        mma(S[kt], ops.kc[0][kt][p], e_h);
-        mma(S[kt], ops.kc[0][kt][p], e_l);
-        mma(S[kt], ops.kc[1][kt][p], e_h);
-      }
+      for (int p = 0; p < 2; ++p) mma(S[kt], ops.kc[kt][p], sE[p][l]);
     }
   };
 
   // three operand buffers in rotation: while chunk c is computed, chunk
   // c+1's operands are in flight and chunk c+2's are being loaded (past the
   // last chunk the last record is read again, so every step issues the same
-  // loads and the compiler's waits stay exact; two buffers of loads stay
-  // below the 63 outstanding vector memory operations a wave can track)
+  // loads and the compiler's waits stay exact)
   Ops<D> bufA, bufB, bufC;
   if (nch > 0) {
     load_ops<D>(bufA, rec_of(0), w, l, g, vt);
