@@ -8,10 +8,11 @@
 //   O = Qg S0 + Bqk E = Qg S0 + Bqk (U - W S0) = Q' S0 + Bqk U,
 //   Q' = Qg - Bqk W          (computed per chunk, in parallel)
 //
-// Kernel 1 (prep) is persistent: each workgroup walks (chunk, head) items
-// and loads the raw inputs of its next item into registers while it
-// computes the current one.  Per item it produces, as MFMA fragments:
-// W, Q' and Kc^T (fp16), U and Bqk U (fp32 accumulator tiles) and e^G[C-1].
+// Kernel 1 (prep) runs one workgroup of four waves per (chunk, head) item,
+// two workgroups per CU, each wave holding 16 tokens of the chunk in
+// registers.  Per item it produces, as MFMA fragments:
+// W, Q' and Kc^T (fp16 fragments), U and Bqk U (fp16 accumulator tiles) and
+// e^G[C-1].
 //
 // Precision (fp32 accumulation throughout).  Inside the prep, an operand
 // whose bf16 rounding would show in the outputs is split into hi + lo bf16
@@ -19,8 +20,9 @@
 // in Q K^T (the intra-chunk matrix Bqk), Bqk itself and U in Bqk U.  The
 // K K^T operands, T and Kg stay single bf16.  The decay-scaled operands
 // there span up to e^(+-80) (the anchor sits mid-chunk), which only bf16
-// covers.  The operands of the sequential pass -- W, Q', Kc, S and E -- are
-// all of moderate size and go through single fp16 (11-bit significand).
+// covers.  The operands of the sequential pass -- W, Q', Kc, U, Bqk U, S and
+// E -- are all of moderate size and go through single fp16 (11-bit
+// significand).
 //
 // Kernel 2 (state pass) is one workgroup per (sequence, head, 16 value
 // columns): S's columns never mix in the recurrence.  Per chunk:
@@ -40,7 +42,7 @@ using HHalf = f16x4;
 using SplitB = Split<PathBF16>;
 constexpr int C = kChunk;
 constexpr size_t FB = 64 * sizeof(Frag);   // bytes per fragment
-constexpr int kPrepThreads = 512;
+constexpr int kPrepThreads = 256;
 
 // Per (chunk slot, head) record.
 template <int D>
@@ -49,483 +51,435 @@ struct Rec {
   static constexpr size_t W = 0;                             // [4 token tiles][KB]          W
   static constexpr size_t QP = W + 4 * KB * FB;              // [4 token tiles][KB]          Q'
   static constexpr size_t KC = QP + 4 * KB * FB;             // [NT key tiles][2]            Kc^T
-  static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f32x4
-  static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 16; // same layout, Bqk U
-  static constexpr size_t G = BU + (size_t)NT * 4 * 64 * 16; // [D] fp32 e^G[C-1]
+  static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f16x4
+  static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 8;  // same layout, Bqk U
+  static constexpr size_t G = BU + (size_t)NT * 4 * 64 * 8;  // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
 
-// Raw inputs of one item held in registers, token-major, as 16-byte vectors
-// (K, Q, V rows in bf16, log_alpha rows in fp32), and beta for one token.
+// LDS plan of the prep workgroup (bytes; two workgroups fit one CU).
+//   region X: Kbar fragments of one stage of key blocks and the Kc^T
+//             fragments; then L, T and L's diagonal blocks for the inverse;
+//             then U (hi, lo) fragments
+//   region Y: Kg^T and V^T fragments; -W fragments replace Kg^T
+//   tile sums of log_alpha and beta
 template <int D>
-struct Prefetch {
-  static constexpr int VR = D / 8;                      // bf16 vectors per row
-  static constexpr int NVT = C * VR / kPrepThreads;     // bf16 vectors per thread and tensor
-  static constexpr int VRA = D / 4;                     // fp32 vectors per row
-  static constexpr int NVA = C * VRA / kPrepThreads;    // fp32 vectors per thread
-  static constexpr int SEGS = kPrepThreads / D;         // token runs per channel (cumulative sum)
-  static constexpr int SL = C / SEGS;                   // tokens per run
-  uint4 k[NVT], q[NVT], v[NVT];
-  f32x4 la[NVA];
-  float beta;
+struct PrepLds {
+  static constexpr int KB = D / 32, NT = D / 16;
+  static constexpr int SB = KB < 2 ? KB : 2;   // key blocks per stage of A and Bqk
+  static constexpr int PL = C + 4;             // fp32 row pitch of L and T
+  static constexpr size_t KBAR = 0;                              // [hi,lo][wave][SB][64]
+  static constexpr size_t KCT = KBAR + 2 * 4 * SB * FB;          // [NT][2][64] fp16
+  static constexpr size_t XL = 0;                                // fp32 [C][PL]
+  static constexpr size_t XT = XL + (size_t)C * PL * 4;          // fp32 [C][PL]
+  static constexpr size_t XLD = XT + (size_t)C * PL * 4;         // fp32 [4][16][20]
+  static constexpr size_t UX = 0;                                // [hi,lo][NT][2][64]
+  static constexpr size_t XEND1 = KCT + NT * 2 * FB;
+  static constexpr size_t XEND2 = XLD + 4 * 16 * 20 * 4;
+  static constexpr size_t XEND3 = UX + 2 * NT * 2 * FB;
+  static constexpr size_t XBYTES = XEND1 > XEND2 ? (XEND1 > XEND3 ? XEND1 : XEND3) : (XEND2 > XEND3 ? XEND2 : XEND3);
+  static constexpr size_t KGT = XBYTES;                          // [NT][2][64]; later -W [NT][2][64]
+  static constexpr size_t VT = KGT + NT * 2 * FB;                // [NT][2][64]
+  static constexpr size_t TOT = VT + NT * 2 * FB;                // fp32 [4][D]
+  static constexpr size_t BETA = TOT + (size_t)4 * D * 4;        // fp32 [C]
+  static constexpr size_t BYTES = BETA + C * 4;
 };
 
-template <int D>
-__device__ __forceinline__ void prefetch(Prefetch<D>& f, const In* __restrict__ q, const In* __restrict__ k,
-                                         const In* __restrict__ v, const float* __restrict__ la,
-                                         const In* __restrict__ beta, int H, int h, int64_t t0, int len,
-                                         int tid) {
-  using F = Prefetch<D>;
-  const int64_t base = (t0 * H + h) * D;   // first element of the item's rows
-  const int pitch = H * D;                 // elements between consecutive tokens
-#pragma unroll
-  for (int i = 0; i < F::NVT; ++i) {
-    const int idx = tid + i * kPrepThreads;
-    const int r = idx / F::VR, cv = idx % F::VR;
-    f.k[i] = f.q[i] = f.v[i] = uint4{0, 0, 0, 0};
-    if (r < len) {
-      const int off = r * pitch + cv * 8;
-      f.k[i] = *reinterpret_cast<const uint4*>(k + base + off);
-      f.q[i] = *reinterpret_cast<const uint4*>(q + base + off);
-      f.v[i] = *reinterpret_cast<const uint4*>(v + base + off);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < F::NVA; ++i) {
-    const int idx = tid + i * kPrepThreads;
-    const int r = idx / F::VRA, cv = idx % F::VRA;
-    f.la[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (r < len) f.la[i] = *reinterpret_cast<const f32x4*>(la + base + r * pitch + cv * 4);
-  }
-  f.beta = (tid < len) ? (float)beta[(t0 + tid) * H + h] : 0.f;
+// Byte offset of element (token r of the wave's tile, column c4 + e) in a
+// [NT column tiles][2 token blocks][64 lanes] fragment array whose fragments
+// hold eight tokens of one column (the B operand of a product over tokens).
+// Row layout: the lane holds token 16 w + l16 and columns c4 + e, c4 a
+// multiple of 4.
+__device__ __forceinline__ int tpos(int w, int l16, int c4, int e) {
+  const int c = c4 + e;
+  return ((((c >> 4) * 2 + (w >> 1)) * 64 + (c & 15) + 16 * (l16 >> 2)) * 16) + 2 * ((l16 & 3) + 4 * (w & 1));
 }
 
-// next (chunk slot, head) item of this workgroup that holds tokens
-__device__ __forceinline__ int64_t next_item(const int32_t* __restrict__ cu, int N, int H, int64_t it,
-                                             int64_t n_items, int& n, int64_t& t0, int& len) {
-  for (; it < n_items; it += gridDim.x)
-    if (decode_slot(cu, N, it / H, n, t0, len)) return it;
-  return n_items;
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {   // lane i of a DPP row gets lane i - N, 0 below the row
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + N, 0xF, 0xF, true));
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: per-chunk factors (persistent).
+// Kernel 1: per-chunk factors, one workgroup of four waves per (chunk slot,
+// head).  Wave w holds tokens [16 w, 16 w + 16) of the chunk in "row layout":
+// lane l has token 16 w + l % 16 and, for key block p, keys
+// 32 p + kpos(l / 16, m), m = 0..7 -- which is at once the A operand of a
+// product over keys and, lane for lane, the accumulator tiles of the
+// transposed (key x token) matrix for key tiles 2p and 2p + 1.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(
+__global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
-    int N, int H, int64_t n_items, unsigned char* __restrict__ ws) {
+    int N, int H, unsigned char* __restrict__ ws) {
   using R = Rec<D>;
-  using F = Prefetch<D>;
-  constexpr int KB = D / 32, NT = D / 16;
-  constexpr int NW = kPrepThreads / 64;
-  constexpr int PI = D + 8;   // bf16 row pitch (+16 bytes)
-  constexpr int PX = D + 4;   // fp32 row pitch (+16 bytes)
-  constexpr int PL = C + 4;
-  constexpr int SEGS = F::SEGS, SL = F::SL;
-  constexpr size_t KBYTES = (size_t)C * PI * 2 > 16 * FB ? (size_t)C * PI * 2 : 16 * FB;
-  constexpr size_t LBYTES = (size_t)C * PL * 4;   // one 64 x 64 fp32 matrix
-  constexpr size_t BIGBYTES = 2 * LBYTES + 8 * FB > 40 * FB ? 2 * LBYTES + 8 * FB : 40 * FB;
+  using L = PrepLds<D>;
+  constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
+  __shared__ __align__(16) unsigned char lds[L::BYTES];
 
-  __shared__ __align__(16) unsigned char sKraw[KBYTES];   // K rows; then Bqk fragments
-  __shared__ __align__(16) In sQ[C][PI];
-  __shared__ __align__(16) float sX[C][PX];               // X = e^(G - G[31])
-  // key-block staging (two buffers of 20 fragments) during P3; afterwards
-  // L = Diag(beta) A (strictly lower), T and the T' fragments
-  __shared__ __align__(16) unsigned char sBig[BIGBYTES];
-  __shared__ __align__(16) Frag sKg[NT][2][64];           // Kg^T fragments (row key, k token)
-  __shared__ __align__(16) In sV[C][PI];                  // V rows
-  __shared__ __align__(16) float sLdT[4][16][20];         // diagonal 16-blocks of L, transposed
-  __shared__ float sEgm[D], sEcm[D], sGm[D], sGc[D], sBeta[C];
-  __shared__ float sSeg[SEGS][D];
-  __shared__ __align__(16) float sScr[4][16][20];
-  auto sK = reinterpret_cast<In (*)[PI]>(sKraw);
-  auto sBq = reinterpret_cast<Frag (*)[4][2][64]>(sKraw);       // [hi,lo][row tile][token block][lane]
-  auto sStage = reinterpret_cast<Frag (*)[20][64]>(sBig);       // [buffer][fragment][lane]
-  auto sL = reinterpret_cast<float (*)[PL]>(sBig);
-  auto sT = reinterpret_cast<float (*)[PL]>(sBig + LBYTES);
-  auto sTf = reinterpret_cast<Frag (*)[2][64]>(sBig + 2 * LBYTES);   // T' [row tile][token block]
-
+  const int64_t item = blockIdx.x;
+  const int64_t slot = item / H;
+  const int h = (int)(item % H);
   int n, len;
   int64_t t0;
-  int64_t item = next_item(cu, N, H, blockIdx.x, n_items, n, t0, len);
-  F pf;
-  if (item < n_items) prefetch<D>(pf, q, k, v, log_alpha, beta, H, (int)(item % H), t0, len, threadIdx.x);
+  if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
+  unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
 
-  while (item < n_items) {
-    // The thread index is re-read through an opaque move each item so that
-    // the many lane-dependent LDS addresses are formed inside the loop
-    // instead of being hoisted out of it and spilled.
-    int tid;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, l16 = l & 15;
-    const int ch = tid % D, sg = tid / D;
-    const int64_t slot = item / H;
-    const int h = (int)(item % H);
-    unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, l16 = l & 15;
+  const int r = 16 * w + l16;   // this lane's token in the chunk
 
-    // ---- P1: prefetched rows to LDS (log_alpha into the X buffer, V into
-    //      its fragments); running sums of log_alpha -------------------------
-#pragma unroll
-    for (int i = 0; i < F::NVT; ++i) {
-      const int idx = tid + i * kPrepThreads;
-      const int r = idx / F::VR, cv = idx % F::VR;
-      *reinterpret_cast<uint4*>(&sK[r][cv * 8]) = pf.k[i];
-      *reinterpret_cast<uint4*>(&sQ[r][cv * 8]) = pf.q[i];
-      *reinterpret_cast<uint4*>(&sV[r][cv * 8]) = pf.v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < F::NVA; ++i) {
-      const int idx = tid + i * kPrepThreads;
-      const int r = idx / F::VRA, cv = idx % F::VRA;
-      *reinterpret_cast<f32x4*>(&sX[r][cv * 4]) = pf.la[i];
-    }
-    if (tid < C) sBeta[tid] = pf.beta;
-    int n2, len2;
-    int64_t t02;
-    const int64_t item2 = next_item(cu, N, H, item + gridDim.x, n_items, n2, t02, len2);
-    __syncthreads();
+  auto sKb = [&](int hl, int wv, int pb) { return reinterpret_cast<Frag*>(lds + L::KBAR) + ((hl * 4 + wv) * SB + pb) * 64; };
+  float* sL = reinterpret_cast<float*>(lds + L::XL);
+  float* sT = reinterpret_cast<float*>(lds + L::XT);
+  float* sLdT = reinterpret_cast<float*>(lds + L::XLD);   // [4][16][20]
+  float* sTot = reinterpret_cast<float*>(lds + L::TOT);
+  float* sBeta = reinterpret_cast<float*>(lds + L::BETA);
 
-    // ---- P2: cumulative log decay; X; Kg^T and Kc^T fragments --------------
-    {
-      float gl[SL];
-      {
-        float run = 0.f;
+  // ---- inputs in row layout --------------------------------------------------
+  bf16x4 kr[KB][2], qr[KB][2], vr[KB][2];
+  f32x4 gr[KB][2];
+  float bt = 0.f;
+  {
+    const bool valid = r < len;
+    const int64_t base = ((t0 + r) * H + h) * D;
 #pragma unroll
-        for (int r = 0; r < SL; ++r) {
-          run += sX[sg * SL + r][ch];
-          gl[r] = run;
+    for (int p = 0; p < KB; ++p)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = 32 * p + 16 * hh + 4 * g;
+        kr[p][hh] = qr[p][hh] = vr[p][hh] = bf16x4{(In)0.f, (In)0.f, (In)0.f, (In)0.f};
+        gr[p][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+          kr[p][hh] = *reinterpret_cast<const bf16x4*>(k + base + key);
+          qr[p][hh] = *reinterpret_cast<const bf16x4*>(q + base + key);
+          vr[p][hh] = *reinterpret_cast<const bf16x4*>(v + base + key);
+          gr[p][hh] = *reinterpret_cast<const f32x4*>(log_alpha + base + key);
         }
-        sSeg[sg][ch] = run;
       }
-      __syncthreads();
-      float off = 0.f;
-      for (int s2 = 0; s2 < sg; ++s2) off += sSeg[s2][ch];
+    if (valid) bt = (float)beta[(t0 + r) * H + h];
+  }
+
+  // ---- A: cumulative log decay over the tokens ---------------------------------
+  // inclusive scan over the 16 tokens of the tile (a DPP row), then the sums
+  // of the earlier tiles from LDS
 #pragma unroll
-      for (int r = 0; r < SL; ++r) gl[r] += off;
-      if (sg == 31 / SL) sGm[ch] = gl[31 % SL];
-      if (sg == SEGS - 1) sGc[ch] = gl[SL - 1];
-      __syncthreads();
-      const float gm = sGm[ch], gc = sGc[ch];
-      const float egm = __expf(gm), ecm = __expf(gc - gm);
-      if (sg == 0) {
-        sEgm[ch] = egm;
-        sEcm[ch] = ecm;
-        reinterpret_cast<float*>(rec + R::G)[ch] = __expf(gc);
+  for (int p = 0; p < KB; ++p)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = gr[p][hh][e];
+        x += row_shr<1>(x);
+        x += row_shr<2>(x);
+        x += row_shr<4>(x);
+        x += row_shr<8>(x);
+        gr[p][hh][e] = x;
       }
-      // this channel is key ch: key tile ch/16, fragment row ch%16.  Four
-      // consecutive tokens j0..j0+3 of a 32-token block sit at fragment
-      // positions 4*hh .. 4*hh+3 of lane row + 16*gp.
-      const int tile = ch >> 4, rowl = ch & 15;
+  if (l16 == 15) {
 #pragma unroll
-      for (int r0 = 0; r0 < SL; r0 += 4) {
-        const int j0 = sg * SL + r0;
-        const int p = j0 >> 5, jj = j0 & 31, gp = (jj & 15) >> 2, hh = jj >> 4;
-        const int lane = rowl + 16 * gp;
-        Half kg4;
-        HHalf kc4;
+    for (int p = 0; p < KB; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + e;
-          const float x = __expf(gl[r0 + e] - gm);
-          sX[j][ch] = x;
-          const float kx = (float)sK[j][ch];
-          kg4[e] = (In)(kx * x * egm);
-          kc4[e] = (_Float16)(kx * __builtin_amdgcn_rcpf(x) * ecm);
-        }
-        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sKg[tile][p][lane]) + 4 * hh) = kg4;
-        const int koff = ((tile * 2 + p) * 64 + lane) * 16 + 8 * hh;
-        *reinterpret_cast<HHalf*>(rec + R::KC + koff) = kc4;
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<f32x4*>(sTot + w * D + 32 * p + 16 * hh + 4 * g) = gr[p][hh];
+  }
+  if (g == 0) sBeta[r] = bt;
+  __syncthreads();
+
+  f32x4 gmv[KB][2], gcv[KB][2];   // G[31] and G[C-1] of this lane's keys
+#pragma unroll
+  for (int p = 0; p < KB; ++p)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int key = 32 * p + 16 * hh + 4 * g;
+      f32x4 t[4];
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) t[wv] = *reinterpret_cast<const f32x4*>(sTot + wv * D + key);
+      f32x4 off = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int wv = 0; wv < 3; ++wv)
+        if (wv < w) off += t[wv];
+      gr[p][hh] += off;
+      gmv[p][hh] = t[0] + t[1];
+      gcv[p][hh] = gmv[p][hh] + t[2] + t[3];
+      if (w == 0 && l16 == 0) {
+        f32x4 eg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) eg[e] = __expf(gcv[p][hh][e]);
+        *reinterpret_cast<f32x4*>(rec + R::G + key * 4) = eg;
       }
     }
-    __syncthreads();
 
-    // ---- P3: A = Ka Kbar^T and Bqk^T = Kbar Qa^T, one key block at a time --
-    {
-      f32x4 accA[2], accB[2];
+  // ---- B: decay-scaled operands --------------------------------------------------
+  //   X = e^(G - G[31]);  Ka = K X, Kbar = K / X, Qa = Q X  (anchored at token 31)
+  //   Kg = K e^G, Qg = Q e^G, Kc = K e^(G[C-1] - G)
+  Frag kaF[KB], kbH[KB], kbL[KB], qaH[KB], qaL[KB];
+  float qg[KB][8];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accB[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < KB; ++p)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * hh + e;
+        const float gm = gmv[p][hh][e];
+        const float dg = gr[p][hh][e] - gm;
+        const float x = __expf(dg), ix = __expf(-dg);
+        const float egm = __expf(gm), ecm = __expf(gcv[p][hh][e] - gm);
+        const float kx = (float)kr[p][hh][e], qx = (float)qr[p][hh][e];
+        const float ka = kx * x, kb = kx * ix, qa = qx * x;
+        kaF[p][m] = (In)ka;
+        kbH[p][m] = (In)kb;
+        kbL[p][m] = (In)(kb - (float)kbH[p][m]);
+        qaH[p][m] = (In)qa;
+        qaL[p][m] = (In)(qa - (float)qaH[p][m]);
+        qg[p][m] = qa * egm;
+        const int pos = tpos(w, l16, 32 * p + 16 * hh + 4 * g, e);
+        *reinterpret_cast<In*>(lds + L::KGT + pos) = (In)(ka * egm);
+        *reinterpret_cast<_Float16*>(lds + L::KCT + pos) = (_Float16)(kb * ecm);
+        *reinterpret_cast<In*>(lds + L::VT + pos) = vr[p][hh][e];
       }
-      // staging slots: 0..3 Ka, 4..7 Kbar hi, 8..11 Kbar lo, 12..15 Qa hi,
-      // 16..19 Qa lo; key block p+1 is built while block p is multiplied
-      // wave w builds half hh = w / 4 (keys 16 hh .. 16 hh + 15 of the block)
-      // of Ka, Kbar and Qa for row tile w % 4, reading K, Q and X once
-      auto build = [&](int p, int buf) {
-        const int rt = w & 3, hh = w >> 2;
-        const int row = 16 * rt + l16, key = 32 * p + 16 * hh + 4 * g;
-        const f32x4 kv = lds4(&sK[row][key]), qv = lds4(&sQ[row][key]);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sX[row][key]);
-        Half ka, kbh, kbl, qah, qal;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = kv[e] * x[e];
-          const float kb = kv[e] * __builtin_amdgcn_rcpf(x[e]);
-          const float qa = qv[e] * x[e];
-          ka[e] = (In)a;
-          kbh[e] = (In)kb;
-          kbl[e] = (In)(kb - (float)kbh[e]);
-          qah[e] = (In)qa;
-          qal[e] = (In)(qa - (float)qah[e]);
-        }
-        auto put = [&](int slot, const Half& hv) {
-          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sStage[buf][slot][l]) + 4 * hh) = hv;
-        };
-        put(rt, ka);
-        put(4 + rt, kbh);
-        put(8 + rt, kbl);
-        put(12 + rt, qah);
-        put(16 + rt, qal);
-      };
-      build(0, 0);
-      __syncthreads();
-      for (int p = 0; p < KB; ++p) {
-        if (p + 1 < KB) build(p + 1, (p + 1) & 1);
-        const int buf = p & 1;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int pi = w + NW * i;
-          if (pi < 10) {
-            const int rt = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-            const int jt = pi - (rt * (rt + 1)) / 2;
-            const Frag kbh = sStage[buf][4 + jt][l], kbl = sStage[buf][8 + jt][l];
-            const Frag qah = sStage[buf][12 + rt][l], qal = sStage[buf][16 + rt][l];
-            mma(accA[i], sStage[buf][rt][l], kbh);   // A[r][j]
-            mma(accB[i], kbh, qah);                  // Bqk^T[j][r]
-            mma(accB[i], kbh, qal);
-            mma(accB[i], kbl, qah);
-          }
-        }
-        __syncthreads();
-      }
-      // A -> Diag(beta) A (strictly lower) in sL; Bqk -> split fragments
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int pi = w + NW * i;
-        if (pi < 10) {
-          const int rt = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-          const int jt = pi - (rt * (rt + 1)) / 2;
-          Half hb, lb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * g + e, j = 16 * jt + l16;
-            const float lv = (j < r) ? sBeta[r] * accA[i][e] : 0.f;
-            sL[r][j] = lv;
-            if (jt == rt) sLdT[rt][l16][4 * g + e] = lv;   // column j of the block as a row
-            // Bqk^T tile: lane holds Bqk[16 rt + l16][16 jt + 4 g + e]
-            const int rr = 16 * rt + l16, jj = 16 * jt + 4 * g + e;
-            const float x = jj <= rr ? accB[i][e] : 0.f;
-            hb[e] = (In)x;
-            lb[e] = (In)(x - (float)hb[e]);
-          }
-          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sBq[0][rt][jt >> 1][l]) + 4 * (jt & 1)) = hb;
-          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sBq[1][rt][jt >> 1][l]) + 4 * (jt & 1)) = lb;
-          if (jt == rt && (rt & 1) == 0) {   // the half above the diagonal block
-            const Half z = {(In)0.f, (In)0.f, (In)0.f, (In)0.f};
-            *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sBq[0][rt][jt >> 1][l]) + 4) = z;
-            *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sBq[1][rt][jt >> 1][l]) + 4) = z;
-          }
-        }
-      }
-    }
-    __syncthreads();
+  for (int pb = 0; pb < SB; ++pb) {
+    sKb(0, w, pb)[l] = kbH[pb];
+    sKb(1, w, pb)[l] = kbL[pb];
+  }
+  __syncthreads();
 
-    // ---- P4: T = (I + L)^-1 ---------------------------------------------------
-    // 16 x 16 diagonal blocks by column-oriented forward substitution, then
-    // block doubling  [[X, 0], [Y, Z]]^-1 = [[X^-1, 0], [-Z^-1 Y X^-1, Z^-1]]
-    // for the 16-blocks (1,0), (3,2) and then the 32-block (1,0).  The block
-    // products run on v_mfma_f32_16x16x4_f32 with the reduction index of
-    // instruction s taken as 4 g + s, so that a row of the left factor is
-    // one 16-byte LDS read and the right factor is an accumulator tile.
-    {
-      // the next item's inputs are in flight from here on (most waves are
-      // idle in this phase)
-      if (item2 < n_items) prefetch<D>(pf, q, k, v, log_alpha, beta, H, (int)(item2 % H), t02, len2, tid);
-      for (int idx = tid; idx < C * PL; idx += kPrepThreads) (&sT[0][0])[idx] = 0.f;
-      const int bk = l >> 4, cc = l & 15;   // wave 0: lane = (block, column)
-      float x[16];
-      if (w == 0) {
+  // ---- C: A = Ka Kbar^T (tiles (w, j)) and Bqk^T = Kbar Qa^T (tiles (j, w)),
+  //      j <= w, in stages of SB key blocks; Kc^T fragments to the record ----
+  for (int i = tid; i < NT * 2 * 64; i += kPrepThreads)
+    reinterpret_cast<HFrag*>(rec + R::KC)[i] = reinterpret_cast<const HFrag*>(lds + L::KCT)[i];
+  f32x4 accA[4], accB[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+  for (int j = 0; j < 4; ++j) accA[j] = accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 15; ++j) {
-          f32x4 colj[4];   // column j of the block: L[r][j], r = 0..15
+  for (int s = 0; s < KB / SB; ++s) {
+    if (s > 0) {
+      __syncthreads();   // every wave is done with the previous stage
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) colj[qd] = *reinterpret_cast<const f32x4*>(&sLdT[bk][j][4 * qd]);
-#pragma unroll
-          for (int r = j + 1; r < 16; ++r) x[r] -= colj[r >> 2][r & 3] * x[j];
-        }
-      }
-      __syncthreads();   // sT cleared
-      if (w == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[16 * bk + r][16 * bk + cc] = x[r];
-      }
-      __syncthreads();
-      const int c = l16;
-      // accumulator tile (rows 4g+e, column c) of block (R, K) of sT
-      auto ctile = [&](int R, int K) {
-        f32x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = sT[16 * R + 4 * g + e][16 * K + c];
-        return t;
-      };
-      // acc += M[16 R + row][16 K + k] * B[k][col] for the 16-block (R, K) of an LDS matrix
-      auto mma_rows = [&](f32x4& acc, const float (*M)[PL], int R, int K, const f32x4& b) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&M[16 * R + l16][16 * K + 4 * g]);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s4], b[s4], acc, 0, 0, 0);
-      };
-      if (w < 2) {   // T(bb, a) = -T(bb, bb) L(bb, a) T(a, a), bb = a + 1
-        const int a = 2 * w, bb = a + 1;
-        f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-        mma_rows(y, sL, bb, a, ctile(a, a));
-        mma_rows(z, sT, bb, bb, y);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[16 * bb + 4 * g + e][16 * a + c] = -z[e];
-      }
-      __syncthreads();
-      // Y = L[32:64, 0:32] T[0:32, 0:32]; T[32:64, 0:32] = -T[32:64, 32:64] Y;
-      // wave w < 4 owns 16-tile (bi, bj)
-      if (w < 4) {
-        const int bi = w >> 1, bj = w & 1;
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = bj; kb < 2; ++kb) mma_rows(y, sL, 2 + bi, kb, ctile(kb, bj));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sScr[w][4 * g + e][c] = y[e];
-      }
-      __syncthreads();
-      if (w < 4) {
-        const int bi = w >> 1, bj = w & 1;
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb <= bi; ++kb) {
-          f32x4 yt;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) yt[e] = sScr[2 * kb + bj][4 * g + e][c];
-          mma_rows(z, sT, 2 + bi, 2 + kb, yt);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[32 + 16 * bi + 4 * g + e][16 * bj + c] = -z[e];
-      }
-      __syncthreads();
-      // T' = T Diag(beta) fragments (row tile rt, token block p), one per wave
-      {
-        const int rt = w >> 1, p = w & 1;
-        float vals[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int j = 32 * p + kpos(g, m);
-          vals[m] = sT[16 * rt + l16][j] * sBeta[j];
-        }
-        sTf[rt][p][l] = make_frag<PathBF16>(vals);
+      for (int pb = 0; pb < SB; ++pb) {
+        sKb(0, w, pb)[l] = kbH[s * SB + pb];
+        sKb(1, w, pb)[l] = kbL[s * SB + pb];
       }
       __syncthreads();
     }
-
-    // ---- P5: W, Q' = Qg - Bqk W, U = T' V, Bqk U -------------------------------
-    for (int task = w; task < 2 * NT; task += NW) {
-      if (task < NT) {
-        const int it = task;   // key tile
-        f32x4 wc[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          f32x4 wt = {0.f, 0.f, 0.f, 0.f};
-          wc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+      if (j > w) break;
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (p > (rt >> 1)) break;   // T'[r][j] = 0 for j > r
-            const Frag tf = sTf[rt][p][l], kg = sKg[it][p][l];
-            mma(wc[rt], tf, kg);   // W[r][i]
-            mma(wt, kg, tf);       // W^T[i][r]
-          }
-          HHalf hw;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hw[e] = (_Float16)wt[e];
-          *reinterpret_cast<HHalf*>(rec + R::W + ((rt * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hw;
-        }
-        // -W^T as the A operand over token block p (from the W tiles 2p, 2p+1)
-        Frag wn[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            wn[p][e] = (In)(-wc[2 * p][e]);
-            wn[p][4 + e] = (In)(-wc[2 * p + 1][e]);
-          }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          // Q'^T tile (key tile it, token tile rt), started from Qg^T
-          const int r = 16 * rt + l16, k0 = 16 * it + 4 * g;
-          const f32x4 q4 = lds4(&sQ[r][k0]);
-          const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sX[r][k0]);
-          f32x4 acc;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = q4[e] * x4[e] * sEgm[k0 + e];
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (p > (rt >> 1)) break;   // Bqk[r][j] = 0 for j > r
-            mma(acc, wn[p], sBq[0][rt][p][l]);
-            mma(acc, wn[p], sBq[1][rt][p][l]);
-          }
-          HHalf hq;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hq[e] = (_Float16)acc[e];
-          const int qo = ((rt * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1);
-          *reinterpret_cast<HHalf*>(rec + R::QP + qo) = hq;
-        }
-      } else {
-        const int ct = task - NT;   // value tile
-        Frag vf[2];                 // V fragments (col value, k token)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int m = 0; m < 8; ++m) vf[p][m] = sV[32 * p + kpos(g, m)][16 * ct + l16];
-        f32x4 uc[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          uc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (p > (rt >> 1)) break;
-            mma(uc[rt], sTf[rt][p][l], vf[p]);
-          }
-          *reinterpret_cast<f32x4*>(rec + R::U + ((ct * 4 + rt) * 64 + l) * 16) = uc[rt];
-        }
-        // U as the B operand over token block p, split
-        SplitB ub[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          float vals[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vals[e] = uc[2 * p][e];
-            vals[4 + e] = uc[2 * p + 1][e];
-          }
-          ub[p] = make_split<PathBF16>(vals);
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          f32x4 bu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (p > (rt >> 1)) break;
-            const Frag bh = sBq[0][rt][p][l], bl = sBq[1][rt][p][l];
-            mma(bu, bh, ub[p].hi);
-            mma(bu, bh, ub[p].lo);
-            mma(bu, bl, ub[p].hi);
-          }
-          *reinterpret_cast<f32x4*>(rec + R::BU + ((ct * 4 + rt) * 64 + l) * 16) = bu;
-        }
+      for (int pb = 0; pb < SB; ++pb) {
+        const int p = s * SB + pb;
+        const Frag bh = (j == w) ? kbH[p] : sKb(0, j, pb)[l];
+        const Frag bl = (j == w) ? kbL[p] : sKb(1, j, pb)[l];
+        mma(accA[j], kaF[p], bh);
+        mma(accB[j], bh, qaH[p]);
+        mma(accB[j], bh, qaL[p]);
+        mma(accB[j], bl, qaH[p]);
       }
     }
-    __syncthreads();   // LDS is reused by the next item
+  }
+  // Bqk as the A operand over tokens (rows: this wave's tokens), split; the
+  // Bqk^T tiles (j, w) are, lane for lane, its fragments
+  Frag bqH[2], bqL[2];
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int j = 2 * pb + hf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (j < w || (j == w && 4 * g + e <= l16)) ? accB[j][e] : 0.f;
+        const In hv = (In)x;
+        bqH[pb][4 * hf + e] = hv;
+        bqL[pb][4 * hf + e] = (In)(x - (float)hv);
+      }
+    }
+  __syncthreads();   // region X is reused for L and T
 
-    item = item2;
-    n = n2;
-    t0 = t02;
-    len = len2;
+  // ---- D: T = (I + L)^-1, L = Diag(beta) A strictly lower ---------------------
+  {
+    f32x4 brow;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) brow[e] = sBeta[16 * w + 4 * g + e];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j > w) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * w + 4 * g + e, jj = 16 * j + l16;
+        const float lv = (jj < rr) ? brow[e] * accA[j][e] : 0.f;
+        sL[rr * PL + jj] = lv;
+        if (j == w) sLdT[(w * 16 + l16) * 20 + 4 * g + e] = lv;   // column jj of the block as a row
+      }
+    }
+  }
+  __syncthreads();
+  // 16 x 16 diagonal blocks by column-oriented forward substitution (wave 0,
+  // lane = (block, column)), then block doubling
+  //   [[X, 0], [Y, Z]]^-1 = [[X^-1, 0], [-Z^-1 Y X^-1, Z^-1]]
+  // for the 16-blocks (1,0), (3,2) and then the 32-block (1,0).  The block
+  // products run on v_mfma_f32_16x16x4_f32 with the reduction index of
+  // instruction s taken as 4 g + s: a row of the left factor is one 16-byte
+  // LDS read and the right factor is an accumulator tile.
+  if (w == 0) {
+    const int bk = l >> 4, cc = l & 15;
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == cc) ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      f32x4 colj[4];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) colj[qd] = *reinterpret_cast<const f32x4*>(sLdT + (bk * 16 + j) * 20 + 4 * qd);
+#pragma unroll
+      for (int rr = j + 1; rr < 16; ++rr) x[rr] -= colj[rr >> 2][rr & 3] * x[j];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sT[(16 * bk + rr) * PL + 16 * bk + cc] = x[rr];
+  }
+  __syncthreads();
+  const int c = l16;
+  auto ctile = [&](int Rb, int Kb) {
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = sT[(16 * Rb + 4 * g + e) * PL + 16 * Kb + c];
+    return t;
+  };
+  auto mma_rows = [&](f32x4& acc, const float* M, int Rb, int Kb, const f32x4& b) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (16 * Rb + l16) * PL + 16 * Kb + 4 * g);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s4], b[s4], acc, 0, 0, 0);
+  };
+  if (w < 2) {   // T(bb, a) = -T(bb, bb) L(bb, a) T(a, a), bb = a + 1
+    const int a = 2 * w, bb = a + 1;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+    mma_rows(y, sL, bb, a, ctile(a, a));
+    mma_rows(z, sT, bb, bb, y);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(16 * bb + 4 * g + e) * PL + 16 * a + c] = -z[e];
+  }
+  __syncthreads();
+  float* sScr = sLdT;   // the diagonal blocks are done with: Y tiles [4][16][20]
+  {   // Y = L[32:64, 0:32] T[0:32, 0:32]; wave w owns 16-tile (bi, bj)
+    const int bi = w >> 1, bj = w & 1;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = bj; kb < 2; ++kb) mma_rows(y, sL, 2 + bi, kb, ctile(kb, bj));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sScr[(w * 16 + 4 * g + e) * 20 + c] = y[e];
+  }
+  __syncthreads();
+  {   // T[32:64, 0:32] = -T[32:64, 32:64] Y
+    const int bi = w >> 1, bj = w & 1;
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb <= bi; ++kb) {
+      f32x4 yt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yt[e] = sScr[((2 * kb + bj) * 16 + 4 * g + e) * 20 + c];
+      mma_rows(z, sT, 2 + bi, 2 + kb, yt);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sT[(32 + 16 * bi + 4 * g + e) * PL + 16 * bj + c] = -z[e];
+  }
+  __syncthreads();
+  // T' = T Diag(beta), this wave's rows, as A fragments over token blocks
+  Frag tf[2];
+#pragma unroll
+  for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int j = 32 * pb + kpos(g, m);
+      tf[pb][m] = (In)((j <= r) ? sT[r * PL + j] * sBeta[j] : 0.f);
+    }
+
+  // ---- E: W = T' Kg (tiles (w, it)) and W^T (tiles (it, w)) -> record W -----
+  const int npb = (w >> 1) + 1;   // token blocks with T'[r][j] != 0
+  Half wneg[NT];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    f32x4 wc = {0.f, 0.f, 0.f, 0.f}, wt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      if (pb >= npb) break;
+      const Frag kg = reinterpret_cast<const Frag*>(lds + L::KGT)[(it * 2 + pb) * 64 + l];
+      mma(wc, tf[pb], kg);
+      mma(wt, kg, tf[pb]);
+    }
+    HHalf hw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hw[e] = (_Float16)wt[e];
+      wneg[it][e] = (In)(-wc[e]);
+    }
+    *reinterpret_cast<HHalf*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hw;
+  }
+  __syncthreads();   // Kg^T and T are no longer read
+
+  // ---- F: -W tiles to LDS (A operand of W^T over tokens); U = T' V -> record,
+  //      and U split to LDS (B operand over tokens) --------------------------------
+#pragma unroll
+  for (int it = 0; it < NT; ++it)
+    *reinterpret_cast<Half*>(lds + L::KGT + ((it * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1)) = wneg[it];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    f32x4 uc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      if (pb >= npb) break;
+      mma(uc, tf[pb], reinterpret_cast<const Frag*>(lds + L::VT)[(ct * 2 + pb) * 64 + l]);
+    }
+    HHalf u16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u16[e] = (_Float16)uc[e];
+    *reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8) = u16;
+    Half uh, ul;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uh[e] = (In)uc[e];
+      ul[e] = (In)(uc[e] - (float)uh[e]);
+    }
+    const size_t off = ((ct * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1);
+    *reinterpret_cast<Half*>(lds + L::UX + off) = uh;
+    *reinterpret_cast<Half*>(lds + L::UX + NT * 2 * FB + off) = ul;
+  }
+  __syncthreads();
+
+  // ---- G: Q'^T = Qg^T - W^T Bqk^T (tiles (it, w)) -> record Q';
+  //      Bqk U (tiles (w, ct)) -> record -------------------------------------------
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = qg[it >> 1][4 * (it & 1) + e];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      if (pb >= npb) break;
+      const Frag wa = reinterpret_cast<const Frag*>(lds + L::KGT)[(it * 2 + pb) * 64 + l];
+      mma(acc, wa, bqH[pb]);
+      mma(acc, wa, bqL[pb]);
+    }
+    HHalf hq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hq[e] = (_Float16)acc[e];
+    *reinterpret_cast<HHalf*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hq;
+  }
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    f32x4 bu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      if (pb >= npb) break;
+      const Frag uh = reinterpret_cast<const Frag*>(lds + L::UX)[(ct * 2 + pb) * 64 + l];
+      const Frag ul = reinterpret_cast<const Frag*>(lds + L::UX + NT * 2 * FB)[(ct * 2 + pb) * 64 + l];
+      mma(bu, bqH[pb], uh);
+      mma(bu, bqH[pb], ul);
+      mma(bu, bqL[pb], uh);
+    }
+    HHalf bu16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bu16[e] = (_Float16)bu[e];
+    *reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8) = bu16;
   }
 }
 
@@ -541,7 +495,7 @@ struct Ops {
   HFrag w[KB];           // W, token tile of this wave
   HFrag qp[KB];          // Q', token tile of this wave
   HFrag kc[KTW][2];      // Kc^T for this wave's key tiles
-  f32x4 u, bu;           // U and Bqk U, token tile of this wave, this slice
+  HHalf u, bu;           // U and Bqk U, token tile of this wave, this slice
   f32x4 gam[KTW];        // e^G[C-1] for this lane's key rows
 };
 
@@ -556,8 +510,8 @@ __device__ __forceinline__ void load_ops_part(Ops<D>& o, const unsigned char* __
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
       o.w[p] = *reinterpret_cast<const HFrag*>(rec + R::W + ((w * O::KB + p) * 64 + l) * 16);
-    o.u = *reinterpret_cast<const f32x4*>(rec + R::U + ((vt * 4 + w) * 64 + l) * 16);
-    o.bu = *reinterpret_cast<const f32x4*>(rec + R::BU + ((vt * 4 + w) * 64 + l) * 16);
+    o.u = *reinterpret_cast<const HHalf*>(rec + R::U + ((vt * 4 + w) * 64 + l) * 8);
+    o.bu = *reinterpret_cast<const HHalf*>(rec + R::BU + ((vt * 4 + w) * 64 + l) * 8);
   } else if (part == 1) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
@@ -637,7 +591,9 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
     __syncthreads();
     load_ops_part<D>(nxt, nrec, 1, w, l, g, vt);
     // token tile w: W S and Q' S
-    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = ops.bu;
+    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
       const HFrag sf = sS[p][l];
@@ -647,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
     // E = U - W S, published as the B operand over tokens
     HHalf eh;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) eh[e] = (_Float16)(ops.u[e] - wsum[e]);
+    for (int e = 0; e < 4; ++e) eh[e] = (_Float16)((float)ops.u[e] - wsum[e]);
     *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[w >> 1][l]) + 4 * (w & 1)) = eh;
     // O = Q' S + Bqk U for token tile w
 #pragma unroll
@@ -697,14 +653,9 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   const int64_t items = slots * A.num_heads;
   if (A.total_tokens > 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    const unsigned grid = (unsigned)(items < cus ? items : cus);
-    hipLaunchKernelGGL((prep_kernel<D>), dim3(grid), dim3(kPrepThreads), 0, stream, (const In*)A.q,
+    hipLaunchKernelGGL((prep_kernel<D>), dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                        (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens,
-                       A.num_seqs, A.num_heads, items, (unsigned char*)A.workspace);
+                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -48,8 +48,8 @@ def test_status_strings_and_version(lib):
 
 def test_workspace_size(lib):
     f = lib.kda_prefill_workspace_size
-    # bf16 record: W, Q', Kc^T (fp16) + U, Bqk U (fp32) + e^G
-    rec_bf16_128 = 3 * 16384 + 32768 + 32768 + 128 * 4
+    # bf16 record: W, Q', Kc^T, U, Bqk U (fp16) + e^G (fp32)
+    rec_bf16_128 = 3 * 16384 + 2 * 16384 + 128 * 4
     assert f(1, 8192, 32, 128, 128, BF16) == (8192 // 64 + 1 + 1) * 32 * rec_bf16_128
     assert f(1, 256, 1, 64, 64, F32) > 0
     assert f(0, 0, 1, 128, 128, BF16) > 0            # one spare slot per head
