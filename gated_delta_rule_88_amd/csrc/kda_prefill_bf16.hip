@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         f32x4 eg;
 #pragma unroll
         for (int e = 0; e < 4; ++e) eg[e] = __expf(gcv[p][hh][e]);
-        *reinterpret_cast<f32x4*>(rec + R::G + key * 4) = eg;
+        __builtin_nontemporal_store(eg, reinterpret_cast<f32x4*>(rec + R::G + key * 4));
       }
     }
 
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   // ---- C: A = Ka Kbar^T (tiles (w, j)) and Bqk^T = Kbar Qa^T (tiles (j, w)),
   //      j <= w, in stages of SB key blocks; Kc^T fragments to the record ----
   for (int i = tid; i < NT * 2 * 64; i += kPrepThreads)
-    reinterpret_cast<HFrag*>(rec + R::KC)[i] = reinterpret_cast<const HFrag*>(lds + L::KCT)[i];
+    __builtin_nontemporal_store(reinterpret_cast<const HFrag*>(lds + L::KCT)[i], reinterpret_cast<HFrag*>(rec + R::KC) + i);
   f32x4 accA[4], accB[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) accA[j] = accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -396,6 +396,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   // ---- E: W = T' Kg (tiles (w, it)) and W^T (tiles (it, w)) -> record W -----
   const int npb = (w >> 1) + 1;   // token blocks with T'[r][j] != 0
   Half wneg[NT];
+  HFrag wrec;   // two key tiles of W, stored as one fragment
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
     f32x4 wc = {0.f, 0.f, 0.f, 0.f}, wt = {0.f, 0.f, 0.f, 0.f};
@@ -406,13 +407,13 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
       mma(wc, tf[pb], kg);
       mma(wt, kg, tf[pb]);
     }
-    HHalf hw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      hw[e] = (_Float16)wt[e];
+      wrec[4 * (it & 1) + e] = (_Float16)wt[e];
       wneg[it][e] = (In)(-wc[e]);
     }
-    *reinterpret_cast<HHalf*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hw;
+    if (it & 1)
+      __builtin_nontemporal_store(wrec, reinterpret_cast<HFrag*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16));
   }
   __syncthreads();   // Kg^T and T are no longer read
 
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf u16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) u16[e] = (_Float16)uc[e];
-    *reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8) = u16;
+    __builtin_nontemporal_store(u16, reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8));
     Half uh, ul;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 
   // ---- G: Q'^T = Qg^T - W^T Bqk^T (tiles (it, w)) -> record Q';
   //      Bqk U (tiles (w, ct)) -> record -------------------------------------------
+  HFrag qrec;   // two key tiles of Q', stored as one fragment
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
     f32x4 acc;
@@ -459,10 +461,10 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
       mma(acc, wa, bqH[pb]);
       mma(acc, wa, bqL[pb]);
     }
-    HHalf hq;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hq[e] = (_Float16)acc[e];
-    *reinterpret_cast<HHalf*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16 + 8 * (it & 1)) = hq;
+    for (int e = 0; e < 4; ++e) qrec[4 * (it & 1) + e] = (_Float16)acc[e];
+    if (it & 1)
+      __builtin_nontemporal_store(qrec, reinterpret_cast<HFrag*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16));
   }
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf bu16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bu16[e] = (_Float16)bu[e];
-    *reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8) = bu16;
+    __builtin_nontemporal_store(bu16, reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8));
   }
 }
 
