@@ -112,6 +112,12 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *
  * A sequence of length 0 produces no outputs and final_state = init_state
  * (or zeros).  total_tokens may be 0.
+ *
+ * Precision of the bf16 path: fp32 accumulation; the sequential pass over
+ * chunks multiplies fp16 operands (the per-chunk factors, the state and the
+ * prediction error), so state entries and values must stay below 6.5e4 in
+ * magnitude -- true for normalised keys and values of order one.  The fp32
+ * path computes with fp32 operands throughout.
  */
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
                               const float* log_alpha, const void* beta,
