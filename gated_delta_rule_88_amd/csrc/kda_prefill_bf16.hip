@@ -82,7 +82,8 @@ struct PrepLds {
   static constexpr size_t VT = KGT + NT * 2 * FB;                // [NT][2][64]
   static constexpr size_t TOT = VT + NT * 2 * FB;                // fp32 [4][D]
   static constexpr size_t BETA = TOT + (size_t)4 * D * 4;        // fp32 [C]
-  static constexpr size_t BYTES = BETA + C * 4;
+  static constexpr size_t EXPK = BETA + C * 4;                   // fp32 [2][D]: e^G[31], e^(G[C-1]-G[31])
+  static constexpr size_t BYTES = EXPK + (size_t)2 * D * 4;
 };
 
 // Byte offset of element (token r of the wave's tile, column c4 + e) in a
@@ -136,6 +137,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   float* sLdT = reinterpret_cast<float*>(lds + L::XLD);   // [4][16][20]
   float* sTot = reinterpret_cast<float*>(lds + L::TOT);
   float* sBeta = reinterpret_cast<float*>(lds + L::BETA);
+  float* sExpK = reinterpret_cast<float*>(lds + L::EXPK);
 
   // ---- inputs in row layout --------------------------------------------------
   bf16x4 kr[KB][2], qr[KB][2], vr[KB][2];
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   if (g == 0) sBeta[r] = bt;
   __syncthreads();
 
-  f32x4 gmv[KB][2], gcv[KB][2];   // G[31] and G[C-1] of this lane's keys
+  f32x4 gmv[KB][2];   // G[31] of this lane's keys
 #pragma unroll
   for (int p = 0; p < KB; ++p)
 #pragma unroll
@@ -202,14 +204,21 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         if (wv < w) off += t[wv];
       gr[p][hh] += off;
       gmv[p][hh] = t[0] + t[1];
-      gcv[p][hh] = gmv[p][hh] + t[2] + t[3];
-      if (w == 0 && l16 == 0) {
-        f32x4 eg;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) eg[e] = __expf(gcv[p][hh][e]);
-        __builtin_nontemporal_store(eg, reinterpret_cast<f32x4*>(rec + R::G + key * 4));
-      }
     }
+  // per-key exponentials, once per key: e^G[31] and e^G[C-1] (threads 0..D-1),
+  // e^(G[C-1] - G[31]) (threads D..2D-1)
+  {
+    const int key = tid % D;
+    const float tm = sTot[key] + sTot[D + key];
+    const float tc = tm + sTot[2 * D + key] + sTot[3 * D + key];
+    if (tid < D) {
+      sExpK[key] = __expf(tm);
+      __builtin_nontemporal_store(__expf(tc), reinterpret_cast<float*>(rec + R::G) + key);
+    } else if (tid < 2 * D) {
+      sExpK[D + key] = __expf(tc - tm);
+    }
+  }
+  __syncthreads();
 
   // ---- B: decay-scaled operands --------------------------------------------------
   //   X = e^(G - G[31]);  Ka = K X, Kbar = K / X, Qa = Q X  (anchored at token 31)
@@ -219,14 +228,17 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 #pragma unroll
   for (int p = 0; p < KB; ++p)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < 2; ++hh) {
+      const int key = 32 * p + 16 * hh + 4 * g;
+      const f32x4 egm4 = *reinterpret_cast<const f32x4*>(sExpK + key);
+      const f32x4 ecm4 = *reinterpret_cast<const f32x4*>(sExpK + D + key);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * hh + e;
         const float gm = gmv[p][hh][e];
         const float dg = gr[p][hh][e] - gm;
         const float x = __expf(dg), ix = __expf(-dg);
-        const float egm = __expf(gm), ecm = __expf(gcv[p][hh][e] - gm);
+        const float egm = egm4[e], ecm = ecm4[e];
         const float kx = (float)kr[p][hh][e], qx = (float)qr[p][hh][e];
         const float ka = kx * x, kb = kx * ix, qa = qx * x;
         kaF[p][m] = (In)ka;
@@ -240,6 +252,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         *reinterpret_cast<_Float16*>(lds + L::KCT + pos) = (_Float16)(kb * ecm);
         *reinterpret_cast<In*>(lds + L::VT + pos) = vr[p][hh][e];
       }
+    }
 #pragma unroll
   for (int pb = 0; pb < SB; ++pb) {
     sKb(0, w, pb)[l] = kbH[pb];
@@ -592,22 +605,23 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
     }
     __syncthreads();
     load_ops_part<D>(nxt, nrec, 1, w, l, g, vt);
-    // token tile w: W S and Q' S
+    // token tile w: W S first -- E gates the other waves -- then Q' S
+    HFrag sf[KB];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) sf[p] = sS[p][l];
     f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
-#pragma unroll
-    for (int p = 0; p < KB; ++p) {
-      const HFrag sf = sS[p][l];
-      mma(wsum, ops.w[p], sf);
-      mma(qsum, ops.qp[p], sf);
-    }
+    for (int p = 0; p < KB; ++p) mma(wsum, ops.w[p], sf[p]);
     // E = U - W S, published as the B operand over tokens
     HHalf eh;
 #pragma unroll
     for (int e = 0; e < 4; ++e) eh[e] = (_Float16)((float)ops.u[e] - wsum[e]);
     *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[w >> 1][l]) + 4 * (w & 1)) = eh;
     // O = Q' S + Bqk U for token tile w
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[p]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + 4 * g + e;
