@@ -221,6 +221,18 @@ def main():
         kda.kda_decode_step(Dd["q"][s], Dd["k"][s], Dd["v"][s], Dd["log_alpha"][s], Dd["beta"][s],
                             state, o=od)
 
+    # the same decode workload through a state pool twice its size, sequences
+    # scattered over the slots by a seeded permutation
+    pool = torch.zeros((2 * dwl.num_seqs,) + tuple(state.shape[1:]), device=dev, dtype=torch.float32)
+    g_perm = torch.Generator().manual_seed(5)
+    sidx = torch.randperm(2 * dwl.num_seqs, generator=g_perm)[:dwl.num_seqs].to(torch.int32).to(dev)
+    pool[sidx.long()] = state
+
+    def decode_pooled(s):
+        s %= n_dec
+        kda.kda_decode_step_pooled(Dd["q"][s], Dd["k"][s], Dd["v"][s], Dd["log_alpha"][s], Dd["beta"][s],
+                                   sidx, pool, o=od)
+
     if args.part in ("prefill", "decode"):
         for s in range(args.warmup + args.steps):
             prefill() if args.part == "prefill" else decode(s)
@@ -244,6 +256,17 @@ def main():
         ev[s][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # pooled decode, timed on its own
+    for s in range(args.warmup):
+        decode_pooled(s)
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for s in range(K):
+        evp[s][0].record()
+        decode_pooled(args.warmup + s)
+        evp[s][1].record()
+    torch.cuda.synchronize()
+    pool_ms = [e[0].elapsed_time(e[1]) for e in evp]
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -293,6 +316,10 @@ def main():
         "decode": {"ms": round(dec_avg, 5), "ms_min": round(min(dec_ms), 5),
                    "value": round(dec_gbps, 1), "unit": "GB/s",
                    "tokens_per_s": round(dwl.num_seqs / (dec_avg * 1e-3), 1), "roofline": roof_dec},
+        "decode_pooled": {"ms": round(sum(pool_ms) / K, 5), "ms_min": round(min(pool_ms), 5),
+                          "value": round(dbytes / (sum(pool_ms) / K * 1e-3) / 1e9, 1), "unit": "GB/s",
+                          "pool_slots": 2 * dwl.num_seqs,
+                          "launch": "kda_decode_step_pooled: decode_step_kernel with a slot map"},
         "roofline": dominant,
     }
     if not args.no_cpu_baseline:

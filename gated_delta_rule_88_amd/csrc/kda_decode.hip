@@ -22,6 +22,7 @@
 // products reduce over the 16 lanes of a DPP row; no LDS and no barrier.
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_prefill_common.h"
 
 namespace kda {
 
@@ -32,13 +33,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, float* __restrict__ state,
-    typename P::In* __restrict__ o) {
+    typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H) {
   using In = typename P::In;
   constexpr int NK = D / 16;        // keys per lane
   constexpr int NC = NK / 4;        // float4 pieces per lane and row
   constexpr int ROWS = D / (kDecodeThreads / 16);   // rows per 16-lane group
 
   const int64_t tok = blockIdx.x;   // n * H + h
+  const int64_t slot = state_slot(sidx, pool_slots, (int)(tok / H));
+  if (slot < 0) return;             // whole workgroup: no state for this sequence
   const int tid = threadIdx.x;
   const int grp = tid >> 4;         // groups of 16 lanes
   const int l16 = tid & 15;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   const float kq = row16_sum(kq_part);
   const float b = to_f32(beta[tok]);
 
-  float* srow0 = state + tok * D * D;
+  float* srow0 = state + (slot * H + tok % H) * D * D;
   f32x4 s[ROWS][NC];
 #pragma unroll
   for (int it = 0; it < ROWS; ++it) {
@@ -109,7 +112,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   const unsigned blocks = (unsigned)((int64_t)A.num_seqs * A.num_heads);
   hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
                      (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
-                     (const In*)A.beta, A.state, (In*)A.o);
+                     (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads);
   return hipGetLastError();
 }
 

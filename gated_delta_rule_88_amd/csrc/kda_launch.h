@@ -16,6 +16,8 @@ struct DecodeArgs {
   void* o;
   int32_t num_seqs, num_heads, d;
   bool bf16;
+  const int32_t* state_indices;   // NULL: sequence n uses state[n]
+  int32_t pool_slots;
 };
 
 struct PrefillArgs {
@@ -31,6 +33,8 @@ struct PrefillArgs {
   int32_t num_heads, d;
   bool bf16;
   void* workspace;
+  const int32_t* state_indices;   // NULL: sequence n uses init_state[n] / final_state[n]
+  int32_t pool_slots;
 };
 
 // Per-chunk factor record of the prefill (bytes) for each precision path,

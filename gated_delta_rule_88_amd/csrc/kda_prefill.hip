@@ -457,7 +457,8 @@ __device__ __forceinline__ void load_ops(ChunkOps<P, D>& o, const unsigned char*
 template <class P, int D>
 __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin,
-    typename P::In* __restrict__ o, const unsigned char* __restrict__ ws) {
+    typename P::In* __restrict__ o, const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx,
+    int pool_slots) {
   using In = typename P::In;
   using Frag = typename P::Frag;
   using Half = typename P::Half;
@@ -484,7 +485,9 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   __shared__ Frag sS[NS][KB][64];   // S as the B operand, hi/lo
   __shared__ Frag sE[NS][2][64];    // E as the B operand, hi/lo
 
-  const int64_t sbase = ((int64_t)n * H + h) * D;   // row (value channel) base of state[n][h]
+  const int64_t sslot = state_slot(sidx, pool_slots, n);
+  if (sslot < 0) init = nullptr, fin = nullptr;
+  const int64_t sbase = (sslot * H + h) * D;   // row (value channel) base of state[slot][h]
   f32x4 S[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
@@ -614,7 +617,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
   const unsigned blocks = (unsigned)(groups * 8 * (D / 16));
   hipLaunchKernelGGL((prefill_state_kernel<P, D>), dim3(blocks), dim3(kThreads), 0, stream,
                      A.cu_seqlens, A.num_seqs, A.num_heads, A.init_state, A.final_state,
-                     (In*)A.o, (const unsigned char*)A.workspace);
+                     (In*)A.o, (const unsigned char*)A.workspace, A.state_indices, A.pool_slots);
   return hipGetLastError();
 }
 

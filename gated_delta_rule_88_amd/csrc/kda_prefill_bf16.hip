@@ -555,7 +555,8 @@ __device__ __forceinline__ void load_ops(Ops<D>& o, const unsigned char* __restr
 template <int D>
 __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restrict__ cu, int N, int H,
                                                          const float* init, float* fin, In* __restrict__ o,
-                                                         const unsigned char* __restrict__ ws) {
+                                                         const unsigned char* __restrict__ ws,
+                                                         const int32_t* __restrict__ sidx, int pool_slots) {
   using R = Rec<D>;
   constexpr int NV = D / 16, KB = D / 32, KTW = D / 64;
 
@@ -578,7 +579,9 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
   __shared__ HFrag sS[KB][64];   // S as the B operand
   __shared__ HFrag sE[2][64];    // E as the B operand
 
-  const int64_t sbase = ((int64_t)n * H + h) * D;
+  const int64_t sslot = state_slot(sidx, pool_slots, n);
+  if (sslot < 0) init = nullptr, fin = nullptr;
+  const int64_t sbase = (sslot * H + h) * D;   // row (value channel) base of state[slot][h]
   f32x4 S[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
@@ -679,7 +682,8 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   const int64_t groups = (pairs + 7) / 8;
   const unsigned blocks = (unsigned)(groups * 8 * (D / 16));
   hipLaunchKernelGGL((state_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
-                     A.num_heads, A.init_state, A.final_state, (In*)A.o, (const unsigned char*)A.workspace);
+                     A.num_heads, A.init_state, A.final_state, (In*)A.o, (const unsigned char*)A.workspace,
+                     A.state_indices, A.pool_slots);
   return hipGetLastError();
 }
 

@@ -31,6 +31,15 @@ __device__ __forceinline__ bool decode_slot(const int32_t* __restrict__ cu, int 
   return true;
 }
 
+// State slot of sequence n: n itself, or state_indices[n] for a state pool
+// of pool_slots entries; -1 when that index is out of range (the sequence's
+// state is then neither read nor written).
+__device__ __forceinline__ int64_t state_slot(const int32_t* __restrict__ sidx, int pool_slots, int n) {
+  if (!sidx) return n;
+  const int s = sidx[n];
+  return (s >= 0 && s < pool_slots) ? s : -1;
+}
+
 // four consecutive inputs of a token-major LDS row as fp32
 __device__ __forceinline__ f32x4 lds4(const __bf16* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);

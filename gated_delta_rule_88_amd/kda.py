@@ -50,6 +50,12 @@ def load(path: str = LIB_PATH):
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
+    lib.kda_prefill_varlen_pooled.restype = ctypes.c_int
+    lib.kda_prefill_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+                                              i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kda_decode_step_pooled.restype = ctypes.c_int
+    lib.kda_decode_step_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                           ctypes.c_int, vp]
     _lib = lib
     return lib
 
@@ -160,4 +166,68 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
                              _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(q.device))
     if st != 0:
         raise KdaError(st, "kda_decode_step")
+    return o
+
+
+def kda_prefill_varlen_pooled(q, k, v, log_alpha, beta, cu_seqlens, state_indices, state_pool, *,
+                              read_initial: bool = True, o=None, workspace=None):
+    """Prefill whose states live in ``state_pool [P,H,dv,dk]`` fp32: sequence n
+    starts from slot ``state_indices[n]`` (int32 ``[N]`` on the GPU) when
+    ``read_initial`` (else from zeros) and its final state is written back to
+    that slot.  Returns ``o``."""
+    lib = load()
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    N = cu_seqlens.shape[0] - 1
+    P = state_pool.shape[0]
+    _check(q, "q", (T, H, dk), dt)
+    _check(k, "k", (T, H, dk), dt)
+    _check(v, "v", (T, H, dv), dt)
+    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32)
+    _check(beta, "beta", (T, H), dt)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    _check(state_indices, "state_indices", (N,), torch.int32)
+    _check(state_pool, "state_pool", (P, H, dv, dk), torch.float32)
+    if o is None:
+        o = torch.empty((T, H, dv), device=q.device, dtype=dt)
+    _check(o, "o", (T, H, dv), dt)
+    need = int(lib.kda_prefill_workspace_size(N, T, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    st = lib.kda_prefill_varlen_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(cu_seqlens), _ptr(state_indices), _ptr(state_pool), P,
+                                       1 if read_initial else 0, _ptr(o), N, T, H, dk, dv, code,
+                                       _ptr(workspace), workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise KdaError(st, "kda_prefill_varlen_pooled")
+    return o
+
+
+def kda_decode_step_pooled(q, k, v, log_alpha, beta, state_indices, state_pool, *, o=None):
+    """One recurrent step on pooled states: sequence n's state is slot
+    ``state_indices[n]`` of ``state_pool [P,H,dv,dk]``, updated in place.
+    Returns ``o [N,H,dv]``."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    P = state_pool.shape[0]
+    _check(q, "q", (N, H, dk), dt)
+    _check(k, "k", (N, H, dk), dt)
+    _check(v, "v", (N, H, dv), dt)
+    _check(log_alpha, "log_alpha", (N, H, dk), torch.float32)
+    _check(beta, "beta", (N, H), dt)
+    _check(state_indices, "state_indices", (N,), torch.int32)
+    _check(state_pool, "state_pool", (P, H, dv, dk), torch.float32)
+    if o is None:
+        o = torch.empty((N, H, dv), device=q.device, dtype=dt)
+    _check(o, "o", (N, H, dv), dt)
+    st = lib.kda_decode_step_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                    _ptr(state_indices), _ptr(state_pool), P, _ptr(o), N, H, dk, dv,
+                                    code, _stream(q.device))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step_pooled")
     return o

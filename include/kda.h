@@ -149,6 +149,50 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            int32_t dk, int32_t dv, kda_dtype dtype,
                            hipStream_t stream);
 
+/*
+ * State-pool forms of the two calls, for a serving engine that keeps every
+ * live sequence's recurrent state in one caller-owned pool and checkpoints
+ * prefixes ("Kimi Delta Attention" §07: the fixed-size state is the whole
+ * per-sequence cache; a prefix is resumed from its saved state).
+ *
+ *   state_indices  [num_seqs] int32 device array: sequence n uses pool slot
+ *                  state_indices[n].  Slots must be distinct within a call.
+ *                  An index outside [0, pool_slots) is skipped on the
+ *                  device: that sequence's state is neither read nor
+ *                  written (prefill still writes its outputs, computed from
+ *                  a zero initial state; decode leaves its outputs as they
+ *                  were).
+ *   state_pool     [pool_slots, num_heads, dv, dk] fp32, same per-slot
+ *                  layout as the state arguments above.
+ *
+ * kda_prefill_varlen_pooled: as kda_prefill_varlen, with the initial state
+ * of sequence n read from its slot when read_initial != 0 (zeros when 0)
+ * and its final state written back to the slot.
+ * kda_decode_step_pooled: as kda_decode_step, with the state of sequence n
+ * read and overwritten in its slot.
+ * Errors as for the plain calls; pool_slots < 0 is KDA_ERR_SHAPE and a NULL
+ * state_indices or state_pool is KDA_ERR_NULL.
+ */
+kda_status kda_prefill_varlen_pooled(const void* q, const void* k, const void* v,
+                                     const float* log_alpha, const void* beta,
+                                     const int32_t* cu_seqlens,
+                                     const int32_t* state_indices,
+                                     float* state_pool, int32_t pool_slots,
+                                     int32_t read_initial, void* o,
+                                     int32_t num_seqs, int64_t total_tokens,
+                                     int32_t num_heads, int32_t dk, int32_t dv,
+                                     kda_dtype dtype,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const void* beta,
+                                  const int32_t* state_indices,
+                                  float* state_pool, int32_t pool_slots, void* o,
+                                  int32_t num_seqs, int32_t num_heads,
+                                  int32_t dk, int32_t dv, kda_dtype dtype,
+                                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

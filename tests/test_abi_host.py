@@ -109,3 +109,45 @@ def test_decode_rejects(lib, over, expect):
 def test_decode_zero_sequences_is_a_no_op(lib):
     # nothing to launch: returns before touching HIP
     assert decode(lib, N=0, q=None, state=None) == OK
+
+
+def prefill_pooled(lib, **over):
+    args = dict(q=P, k=P, v=P, la=P, beta=P, cu=P, idx=P, pool=P, slots=4, read=1, o=P, N=1, T=128,
+                H=2, dk=128, dv=128, dtype=BF16, ws=P, wsb=1 << 40, stream=None)
+    args.update(over)
+    return lib.kda_prefill_varlen_pooled(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                         args["cu"], args["idx"], args["pool"], args["slots"],
+                                         args["read"], args["o"], args["N"], args["T"], args["H"],
+                                         args["dk"], args["dv"], args["dtype"], args["ws"],
+                                         args["wsb"], args["stream"])
+
+
+def decode_pooled(lib, **over):
+    args = dict(q=P, k=P, v=P, la=P, beta=P, idx=P, pool=P, slots=8, o=P, N=4, H=2, dk=128, dv=128,
+                dtype=BF16, stream=None)
+    args.update(over)
+    return lib.kda_decode_step_pooled(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                      args["idx"], args["pool"], args["slots"], args["o"], args["N"],
+                                      args["H"], args["dk"], args["dv"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(idx=None), NULL), (dict(pool=None), NULL), (dict(cu=None), NULL), (dict(q=None), NULL),
+    (dict(slots=-1), SHAPE), (dict(N=0), SHAPE), (dict(dk=96, dv=96), UNSUP), (dict(dtype=3), DTYPE),
+    (dict(idx=MIS), ALIGN), (dict(pool=MIS), ALIGN), (dict(ws=None), WS),
+])
+def test_prefill_pooled_rejects(lib, over, expect):
+    assert prefill_pooled(lib, **over) == expect
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(idx=None), NULL), (dict(pool=None), NULL), (dict(o=None), NULL), (dict(slots=-2), SHAPE),
+    (dict(N=-1), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(dtype=9), DTYPE), (dict(idx=MIS), ALIGN),
+    (dict(pool=MIS), ALIGN),
+])
+def test_decode_pooled_rejects(lib, over, expect):
+    assert decode_pooled(lib, **over) == expect
+
+
+def test_decode_pooled_zero_sequences_is_a_no_op(lib):
+    assert decode_pooled(lib, N=0, q=None, idx=None, pool=None) == OK

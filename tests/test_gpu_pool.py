@@ -1,0 +1,146 @@
+"""GPU parity of the state-pool calls (kda_prefill_varlen_pooled,
+kda_decode_step_pooled) against the fp64 oracle.
+
+The pool is indexing only: the oracle runs on the states gathered from the
+pool slots, and the kernels must match it while leaving every slot that no
+sequence names bit-identical, and skip out-of-range indices without touching
+memory.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_88_amd import inputs, kda
+from tests.parity import TOL, row_rel_err, state_rel_err
+from tests.test_gpu_prefill import make_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _pool(P, H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return 0.02 * torch.randn((P, H, D, D), generator=g)
+
+
+def _prefill_pooled(d, idx, pool, read_initial):
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    pool_dev = pool.to(DEV)
+    o = kda.kda_prefill_varlen_pooled(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["cu_seqlens"],
+                                      torch.tensor(idx, dtype=torch.int32, device=DEV), pool_dev,
+                                      read_initial=read_initial)
+    torch.cuda.synchronize()
+    return o, pool_dev.cpu()
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
+@pytest.mark.parametrize("read_initial", [True, False], ids=["resume", "fresh"])
+def test_prefill_pooled(dtype, D, read_initial):
+    lengths = [100, 0, 257]
+    d = make_case(lengths, H=2, D=D, dtype=dtype, seed=31 + D, init_std=0.0)
+    P, idx = 7, [5, 1, 3]
+    pool = _pool(P, 2, D, seed=5)
+    o, after = _prefill_pooled(d, idx, pool, read_initial)
+    init = pool[idx] if read_initial else None
+    ro, rf = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"].long(), init)
+    eo, es = row_rel_err(o, ro), state_rel_err(after[idx], rf)
+    print(f"pooled prefill {dtype} D={D} read_initial={read_initial}: o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    untouched = [s for s in range(P) if s not in idx]
+    assert torch.equal(after[untouched], pool[untouched])
+
+
+def test_prefill_pooled_out_of_range_indices_are_skipped():
+    lengths = [70, 130, 64]
+    d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=44, init_std=0.0)
+    P, idx = 4, [2, -1, 4]          # sequence 1 and 2 name no valid slot
+    pool = _pool(P, 2, 128, seed=6)
+    o, after = _prefill_pooled(d, idx, pool, read_initial=True)
+    # sequence 0 resumes from slot 2; 1 and 2 run from zero states and store nothing
+    init = torch.zeros((3, 2, 128, 128))
+    init[0] = pool[2]
+    ro, rf = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"].long(), init)
+    assert row_rel_err(o, ro) <= TOL[torch.bfloat16]
+    assert state_rel_err(after[2:3], rf[0:1]) <= TOL[torch.bfloat16]
+    assert torch.equal(after[[0, 1, 3]], pool[[0, 1, 3]])
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
+def test_decode_pooled(dtype, D):
+    wl = inputs.WORKLOADS["decode_256"].replace(num_seqs=4, heads=3, dk=D, dv=D,
+                                                dtype="f32" if dtype == torch.float32 else "bf16")
+    d = inputs.decode_inputs(wl, steps=4)
+    P, idx = 9, [8, 0, 3, 5]
+    pool = _pool(P, 3, D, seed=7)
+    pool[idx] = d["state"]
+    pool_dev = pool.to(DEV)
+    sidx = torch.tensor(idx, dtype=torch.int32, device=DEV)
+    ref = d["state"].double().numpy()
+    for s in range(4):
+        args = [d[k][s] for k in ("q", "k", "v", "log_alpha", "beta")]
+        o = kda.kda_decode_step_pooled(*[a.to(DEV) for a in args], sidx, pool_dev)
+        torch.cuda.synchronize()
+        ro, ref = oracle.decode_step(*args, ref)
+        eo = row_rel_err(o, ro)
+        es = state_rel_err(pool_dev.cpu()[idx], ref)
+        print(f"pooled decode {dtype} D={D} step {s}: o {eo:.3e} state {es:.3e}", flush=True)
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+    untouched = [s for s in range(P) if s not in idx]
+    assert torch.equal(pool_dev.cpu()[untouched], pool[untouched])
+
+
+def test_decode_pooled_out_of_range_index_leaves_output_and_pool():
+    wl = inputs.WORKLOADS["decode_256"].replace(num_seqs=3, heads=2)
+    d = inputs.decode_inputs(wl, steps=1)
+    P, idx = 3, [1, 3, 0]           # sequence 1 names no valid slot
+    pool = _pool(P, 2, 128, seed=8)
+    pool[[1, 0]] = d["state"][[0, 2]]
+    pool_dev = pool.to(DEV)
+    o = torch.full((3, 2, 128), 7.0, device=DEV, dtype=torch.bfloat16)
+    args = [d[k][0] for k in ("q", "k", "v", "log_alpha", "beta")]
+    kda.kda_decode_step_pooled(*[a.to(DEV) for a in args], torch.tensor(idx, dtype=torch.int32, device=DEV),
+                               pool_dev, o=o)
+    torch.cuda.synchronize()
+    assert torch.all(o[1] == 7.0)
+    ro, rs = oracle.decode_step(*args, d["state"].double().numpy())
+    assert row_rel_err(o[[0, 2]], ro[[0, 2]]) <= TOL[torch.bfloat16]
+    assert state_rel_err(pool_dev.cpu()[[1, 0]], rs[[0, 2]]) <= TOL[torch.bfloat16]
+    assert torch.equal(pool_dev.cpu()[2], pool[2])
+
+
+def test_prefill_then_decode_through_the_pool():
+    """prefill writes its final states into slots; decode steps continue them
+    there; the whole is the recurrence over prompt + decoded tokens"""
+    lengths = [90, 200]
+    H, D, steps = 2, 128, 3
+    d = make_case(lengths, H=H, D=D, dtype=torch.bfloat16, seed=61, init_std=0.0)
+    wl = inputs.WORKLOADS["decode_256"].replace(num_seqs=2, heads=H, seed=62)
+    dd = inputs.decode_inputs(wl, steps=steps)
+    P, idx = 5, [4, 2]
+    pool = torch.zeros((P, H, D, D))
+    _, after = _prefill_pooled(d, idx, pool, read_initial=False)
+    pool_dev = after.to(DEV)
+    sidx = torch.tensor(idx, dtype=torch.int32, device=DEV)
+    outs = []
+    for s in range(steps):
+        args = [dd[k][s].to(DEV) for k in ("q", "k", "v", "log_alpha", "beta")]
+        outs.append(kda.kda_decode_step_pooled(*args, sidx, pool_dev).cpu())
+    torch.cuda.synchronize()
+    # oracle: each sequence's prompt followed by its decoded tokens
+    q, k, v, la, b, rows = [], [], [], [], [], []
+    cu = [0]
+    for n, L in enumerate(lengths):
+        s0 = int(d["cu_seqlens"][n])
+        parts = [(d[x][s0:s0 + L]) for x in ("q", "k", "v", "log_alpha", "beta")]
+        dec = [torch.stack([dd[x][s][n] for s in range(steps)]) for x in ("q", "k", "v", "log_alpha", "beta")]
+        for lst, a, bb in zip((q, k, v, la, b), parts, dec):
+            lst.append(torch.cat([a, bb]))
+        rows += [cu[-1] + L + s for s in range(steps)]
+        cu.append(cu[-1] + L + steps)
+    ro, rf = oracle.prefill(torch.cat(q), torch.cat(k), torch.cat(v), torch.cat(la), torch.cat(b),
+                            torch.tensor(cu, dtype=torch.int64), None)
+    got = torch.stack([torch.stack([outs[s][n] for s in range(steps)]) for n in range(len(lengths))])
+    want = np.stack([ro[rows[n * steps:(n + 1) * steps]] for n in range(len(lengths))])
+    assert row_rel_err(got, want) <= TOL[torch.bfloat16]
+    assert state_rel_err(pool_dev.cpu()[idx], rf) <= TOL[torch.bfloat16]
