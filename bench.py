@@ -64,6 +64,13 @@ def prefill_algorithmic(T, H, d, n_seqs, init, final):
     return T * H * per_tok + state, T * H * flops_per_tok
 
 
+def gdn_prefill_algorithmic(T, H, d, n_seqs, final):
+    """Bytes of one Gated DeltaNet prefill call: as the KDA call but one fp32
+    gate per token-head."""
+    per_tok = 3 * d * 2 + 4 + 2 + d * 2
+    return T * H * per_tok + d * d * 4 * n_seqs * H * (1 if final else 0)
+
+
 def decode_algorithmic(N, H, d):
     """Bytes of one decode step: state read + write (fp32), q, k, v, o (bf16),
     log_alpha (fp32), beta (bf16)."""
@@ -257,6 +264,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Gated DeltaNet prefill (one gate per token and head) on the same shape
+    la_scalar = P["log_alpha"][..., 0].contiguous()
+
+    def gdn_prefill():
+        kda.gdn_prefill_varlen(P["q"], P["k"], P["v"], la_scalar, P["beta"], P["cu_seqlens"],
+                               None, o=o, final_state=fin, workspace=ws)
+
+    for s in range(args.warmup):
+        gdn_prefill()
+        decode(s)
+    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for s in range(K):
+        evg[s][0].record()
+        gdn_prefill()
+        evg[s][1].record()
+        decode(args.warmup + s)   # streams the caches between calls, as in the main loop
+    torch.cuda.synchronize()
+    gdn_ms = [e[0].elapsed_time(e[1]) for e in evg]
+
     # pooled decode, timed on its own
     for s in range(args.warmup):
         decode_pooled(s)
@@ -316,6 +342,12 @@ def main():
         "decode": {"ms": round(dec_avg, 5), "ms_min": round(min(dec_ms), 5),
                    "value": round(dec_gbps, 1), "unit": "GB/s",
                    "tokens_per_s": round(dwl.num_seqs / (dec_avg * 1e-3), 1), "roofline": roof_dec},
+        "gdn_prefill": {"ms": round(sum(gdn_ms) / K, 5), "ms_min": round(min(gdn_ms), 5),
+                        "tokens_per_s": round(T / (sum(gdn_ms) / K * 1e-3), 1),
+                        "GB_s": round(gdn_prefill_algorithmic(T, H, D, 1, True) / (sum(gdn_ms) / K * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(gdn_prefill_algorithmic(T, H, D, 1, True) / (sum(gdn_ms) / K * 1e-3)
+                                          / 1e9 / HBM_PEAK_GBPS, 4),
+                        "launch": "kda_gdn_prefill_varlen: prep_kernel then state_kernel, one gate per token-head"},
         "decode_pooled": {"ms": round(sum(pool_ms) / K, 5), "ms_min": round(min(pool_ms), 5),
                           "value": round(dbytes / (sum(pool_ms) / K * 1e-3) / 1e9, 1), "unit": "GB/s",
                           "pool_slots": 2 * dwl.num_seqs,

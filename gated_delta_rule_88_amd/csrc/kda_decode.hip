@@ -33,7 +33,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, float* __restrict__ state,
-    typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H) {
+    typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H,
+    int scalar_gate) {
   using In = typename P::In;
   constexpr int NK = D / 16;        // keys per lane
   constexpr int NC = NK / 4;        // float4 pieces per lane and row
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t base = tok * D + c * 64 + 4 * l16;
-    const f32x4 la = *reinterpret_cast<const f32x4*>(log_alpha + base);
+    const f32x4 la = scalar_gate ? f32x4{log_alpha[tok], log_alpha[tok], log_alpha[tok], log_alpha[tok]}
+                                 : *reinterpret_cast<const f32x4*>(log_alpha + base);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float ai = __expf(la[e]);
@@ -112,7 +114,8 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   const unsigned blocks = (unsigned)((int64_t)A.num_seqs * A.num_heads);
   hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
                      (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
-                     (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads);
+                     (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads,
+                     (int)A.scalar_gate);
   return hipGetLastError();
 }
 

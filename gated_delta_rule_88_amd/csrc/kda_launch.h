@@ -18,6 +18,7 @@ struct DecodeArgs {
   bool bf16;
   const int32_t* state_indices;   // NULL: sequence n uses state[n]
   int32_t pool_slots;
+  bool scalar_gate;               // log_alpha holds one gate per (sequence, head)
 };
 
 struct PrefillArgs {
@@ -35,6 +36,7 @@ struct PrefillArgs {
   void* workspace;
   const int32_t* state_indices;   // NULL: sequence n uses init_state[n] / final_state[n]
   int32_t pool_slots;
+  bool scalar_gate;               // log_alpha holds one gate per (token, head)
 };
 
 // Per-chunk factor record of the prefill (bytes) for each precision path,

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, const int32_t* __restrict__ cu, int N, int H,
-    unsigned char* __restrict__ ws) {
+    unsigned char* __restrict__ ws, int scalar_gate) {
   using In = typename P::In;
   using Frag = typename P::Frag;
   using Half = typename P::Half;
@@ -149,7 +149,8 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
 #pragma unroll
     for (int r = 0; r < SL; ++r) {
       const int tok = s * SL + r;
-      const float x = tok < len ? log_alpha[((t0 + tok) * H + h) * D + i] : 0.f;
+      const int64_t th = (t0 + tok) * H + h;
+      const float x = tok < len ? log_alpha[scalar_gate ? th : th * D + i] : 0.f;
       run += x;
       gl[r] = run;
     }
@@ -608,7 +609,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_prep_kernel<P, D>), dim3((unsigned)slots, (unsigned)A.num_heads),
                        dim3(kPrepThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
                        A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads,
-                       (unsigned char*)A.workspace);
+                       (unsigned char*)A.workspace, (int)A.scalar_gate);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

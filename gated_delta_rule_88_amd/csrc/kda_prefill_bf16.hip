@@ -113,7 +113,7 @@ template <int D>
 __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
-    int N, int H, unsigned char* __restrict__ ws) {
+    int N, int H, unsigned char* __restrict__ ws, int scalar_gate) {
   using R = Rec<D>;
   using L = PrepLds<D>;
   constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
@@ -146,6 +146,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   {
     const bool valid = r < len;
     const int64_t base = ((t0 + r) * H + h) * D;
+    // one gate per (token, head): the same log decay for every key channel
+    const float g1 = (valid && scalar_gate) ? log_alpha[(t0 + r) * H + h] : 0.f;
 #pragma unroll
     for (int p = 0; p < KB; ++p)
 #pragma unroll
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
           kr[p][hh] = *reinterpret_cast<const bf16x4*>(k + base + key);
           qr[p][hh] = *reinterpret_cast<const bf16x4*>(q + base + key);
           vr[p][hh] = *reinterpret_cast<const bf16x4*>(v + base + key);
-          gr[p][hh] = *reinterpret_cast<const f32x4*>(log_alpha + base + key);
+          gr[p][hh] = scalar_gate ? f32x4{g1, g1, g1, g1}
+                                  : *reinterpret_cast<const f32x4*>(log_alpha + base + key);
         }
       }
     if (valid) bt = (float)beta[(t0 + r) * H + h];
@@ -674,7 +677,7 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   if (A.total_tokens > 0) {
     hipLaunchKernelGGL((prep_kernel<D>), dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                        (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens,
-                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace);
+                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace, (int)A.scalar_gate);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -50,6 +50,11 @@ def load(path: str = LIB_PATH):
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
+    for name in ("kda_gdn_prefill_varlen",):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.kda_prefill_varlen.argtypes
+    lib.kda_gdn_decode_step.restype = ctypes.c_int
+    lib.kda_gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
     lib.kda_prefill_varlen_pooled.restype = ctypes.c_int
     lib.kda_prefill_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                               i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
@@ -105,6 +110,20 @@ def workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv
 
 def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
                        o=None, final_state=None, want_final: bool = True, workspace=None):
+    return _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, o=o, final_state=final_state,
+                    want_final=want_final, workspace=workspace, scalar_gate=False)
+
+
+def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
+                       o=None, final_state=None, want_final: bool = True, workspace=None):
+    """Gated DeltaNet prefill: as :func:`kda_prefill_varlen` with one gate per
+    (token, head), ``log_alpha [T,H]`` fp32."""
+    return _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, o=o, final_state=final_state,
+                    want_final=want_final, workspace=workspace, scalar_gate=True)
+
+
+def _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, *, o, final_state, want_final,
+             workspace, scalar_gate):
     """Chunked prefill over packed sequences; returns ``(o, final_state)``.
 
     q, k ``[T,H,dk]``; v ``[T,H,dv]`` (bf16 or fp32, one dtype); log_alpha
@@ -121,7 +140,7 @@ def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
     _check(q, "q", (T, H, dk), dt)
     _check(k, "k", (T, H, dk), dt)
     _check(v, "v", (T, H, dv), dt)
-    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32)
+    _check(log_alpha, "log_alpha", (T, H) if scalar_gate else (T, H, dk), torch.float32)
     _check(beta, "beta", (T, H), dt)
     _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
     if init_state is not None:
@@ -136,18 +155,29 @@ def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
     need = int(lib.kda_prefill_workspace_size(N, T, H, dk, dv, code))
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(cu_seqlens), _ptr(init_state), _ptr(o), _ptr(final_state),
-                                N, T, H, dk, dv, code, _ptr(workspace), workspace.numel(),
-                                _stream(q.device))
+    name = "kda_gdn_prefill_varlen" if scalar_gate else "kda_prefill_varlen"
+    st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                            _ptr(cu_seqlens), _ptr(init_state), _ptr(o), _ptr(final_state),
+                            N, T, H, dk, dv, code, _ptr(workspace), workspace.numel(),
+                            _stream(q.device))
     if st != 0:
-        raise KdaError(st, "kda_prefill_varlen")
+        raise KdaError(st, name)
     return o, final_state
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
     """One recurrent step; ``state [N,H,dv,dk]`` fp32 is updated in place.
     Returns ``o [N,H,dv]``."""
+    return _decode(q, k, v, log_alpha, beta, state, o=o, scalar_gate=False)
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
+    """Gated DeltaNet decode step: ``log_alpha [N,H]`` fp32, one gate per
+    (sequence, head); otherwise as :func:`kda_decode_step`."""
+    return _decode(q, k, v, log_alpha, beta, state, o=o, scalar_gate=True)
+
+
+def _decode(q, k, v, log_alpha, beta, state, *, o, scalar_gate):
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -156,16 +186,17 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
     _check(q, "q", (N, H, dk), dt)
     _check(k, "k", (N, H, dk), dt)
     _check(v, "v", (N, H, dv), dt)
-    _check(log_alpha, "log_alpha", (N, H, dk), torch.float32)
+    _check(log_alpha, "log_alpha", (N, H) if scalar_gate else (N, H, dk), torch.float32)
     _check(beta, "beta", (N, H), dt)
     _check(state, "state", (N, H, dv, dk), torch.float32)
     if o is None:
         o = torch.empty((N, H, dv), device=q.device, dtype=dt)
     _check(o, "o", (N, H, dv), dt)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(q.device))
+    name = "kda_gdn_decode_step" if scalar_gate else "kda_decode_step"
+    st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                            _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(q.device))
     if st != 0:
-        raise KdaError(st, "kda_decode_step")
+        raise KdaError(st, name)
     return o
 
 

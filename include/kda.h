@@ -150,6 +150,37 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            hipStream_t stream);
 
 /*
+ * Gated DeltaNet forms of the two calls: one decay gate per (token, head)
+ * instead of one per key channel -- the scalar-gated delta rule that the
+ * "Kimi Delta Attention" page (§02-§03) refines into KDA by giving every key
+ * dimension its own gate.  With a scalar gate, alpha (I - beta k k^T) S =
+ * (I - beta k k^T) alpha S, so the recurrence is KDA's with alpha_t[i] equal
+ * for all i.  Arguments, layouts and errors as for the KDA calls, except:
+ *
+ *   log_alpha  [total_tokens, num_heads] fp32   (kda_gdn_prefill_varlen)
+ *   log_alpha  [num_seqs, num_heads]     fp32   (kda_gdn_decode_step)
+ *
+ * The workspace is kda_prefill_workspace_size(...) as for KDA.
+ */
+kda_status kda_gdn_prefill_varlen(const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const void* beta,
+                                  const int32_t* cu_seqlens,
+                                  const float* init_state,
+                                  void* o, float* final_state,
+                                  int32_t num_seqs, int64_t total_tokens,
+                                  int32_t num_heads, int32_t dk, int32_t dv,
+                                  kda_dtype dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v,
+                               const float* log_alpha, const void* beta,
+                               float* state, void* o,
+                               int32_t num_seqs, int32_t num_heads,
+                               int32_t dk, int32_t dv, kda_dtype dtype,
+                               hipStream_t stream);
+
+/*
  * State-pool forms of the two calls, for a serving engine that keeps every
  * live sequence's recurrent state in one caller-owned pool and checkpoints
  * prefixes ("Kimi Delta Attention" §07: the fixed-size state is the whole

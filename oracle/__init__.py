@@ -13,6 +13,11 @@ compiles it with gcc on first use, marshals arrays and exposes two calls:
 * :func:`decode_step` -- one token per (sequence, head): exactly one loop
   iteration of the same recurrence (the "fused recurrent" decode mode of §06).
 
+:func:`prefill_scalar_gate` and :func:`decode_step_scalar_gate` take one gate
+per (token, head) -- the scalar-gated delta rule (Gated DeltaNet) that §02-§03
+refine into KDA -- and run the same recurrence with that gate repeated over
+the key channels; they add indexing only, no arithmetic.
+
 Inputs may be numpy arrays or torch CPU tensors in float64, float32 or
 bfloat16; they are converted to fp64 exactly inside the C code.
 """
@@ -191,3 +196,22 @@ def decode_step(q, k, v, log_alpha, beta, state, *, nthreads: int | None = None,
     N = qa.shape[0]
     cu = np.arange(N + 1, dtype=np.int64)
     return prefill(q, k, v, log_alpha, beta, cu, state, nthreads=nthreads, lib=lib)
+
+
+def _repeat_gate(log_alpha, dk: int):
+    """``[..., H]`` gates -> ``[..., H, dk]``: the same log decay on every key
+    channel, in the gate's own precision."""
+    a, code = _typed(log_alpha, allow=(F32, F64))
+    return np.ascontiguousarray(np.repeat(a[..., None], dk, axis=-1))
+
+
+def prefill_scalar_gate(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, **kw):
+    """:func:`prefill` with ``log_alpha [T,H]`` (one gate per token and head)."""
+    dk = _typed(q)[0].shape[-1]
+    return prefill(q, k, v, _repeat_gate(log_alpha, dk), beta, cu_seqlens, init_state, **kw)
+
+
+def decode_step_scalar_gate(q, k, v, log_alpha, beta, state, **kw):
+    """:func:`decode_step` with ``log_alpha [N,H]``."""
+    dk = _typed(q)[0].shape[-1]
+    return decode_step(q, k, v, _repeat_gate(log_alpha, dk), beta, state, **kw)

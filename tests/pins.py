@@ -283,6 +283,43 @@ def check_continuation_and_packing(lib, seed=10):
     assert np.array_equal(f[1], s0[1])
 
 
+# --------------------------------------------------------------------------
+# 12. Scalar gate (Gated DeltaNet): the literal scalar-gated delta rule
+#     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+#     gate applied outside the erase, in exact rationals
+# --------------------------------------------------------------------------
+def _brute_force_gdn_exact(alpha, beta, k, v, q, S0):
+    T, dk, dv = len(alpha), len(S0), len(S0[0])
+    S = [row[:] for row in S0]
+    outs = []
+    for t in range(T):
+        E = [[(1 if i == c else 0) - beta[t] * k[t][i] * k[t][c] for c in range(dk)] for i in range(dk)]
+        S = [[alpha[t] * sum(E[i][c] * S[c][j] for c in range(dk)) + beta[t] * k[t][i] * v[t][j]
+              for j in range(dv)] for i in range(dk)]
+        outs.append([sum(S[i][j] * q[t][i] for i in range(dk)) for j in range(dv)])
+    return outs, S
+
+
+def check_scalar_gate_exact(lib, seed=13):
+    rnd = random.Random(seed)
+    for dk, dv, T in ((3, 2, 5), (2, 4, 6)):
+        fr = lambda lo, hi, den: Fraction(rnd.randint(lo, hi), den)
+        alpha = [fr(1, 9, 10) for _ in range(T)]
+        beta = [fr(0, 8, 8) for _ in range(T)]
+        k = [[fr(-4, 4, 8) for _ in range(dk)] for _ in range(T)]
+        q = [[fr(-4, 4, 4) for _ in range(dk)] for _ in range(T)]
+        v = [[fr(-6, 6, 3) for _ in range(dv)] for _ in range(T)]
+        S0 = [[fr(-5, 5, 5) for _ in range(dv)] for _ in range(dk)]
+        outs, S = _brute_force_gdn_exact(alpha, beta, k, v, q, S0)
+        f = lambda M: np.array([[float(x) for x in row] for row in M])
+        la = np.log(np.array([float(a) for a in alpha]))[:, None]          # [T, H=1]
+        o, fin = oracle.prefill_scalar_gate(f(q)[:, None, :], f(k)[:, None, :], f(v)[:, None, :], la,
+                                            np.array([float(b) for b in beta])[:, None],
+                                            np.array([0, T], dtype=np.int64), f(S0).T[None, None], lib=lib)
+        assert _rel(o[:, 0, :], f(outs)) < 1e-12, ("scalar gate outputs vs exact", dk, dv)
+        assert _rel(fin[0, 0], f(S).T) < 1e-12, ("scalar gate state vs exact", dk, dv)
+
+
 ALL_CHECKS = [
     check_exact_bruteforce,
     check_golden_worked_example,
@@ -295,4 +332,5 @@ ALL_CHECKS = [
     check_linearity,
     check_column_permutation,
     check_continuation_and_packing,
+    check_scalar_gate_exact,
 ]
