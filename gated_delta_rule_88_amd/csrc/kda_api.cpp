@@ -25,7 +25,7 @@ kda_status prefill_plain(const void* q, const void* k, const void* v,
                               void* o, float* final_state, int32_t num_seqs,
                               int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                               kda_dtype dtype, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, bool scalar_gate) {
+                              hipStream_t stream, bool scalar_gate, bool raw) {
   kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
   if (st != KDA_OK) return st;
   if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return KDA_ERR_SHAPE;
@@ -42,7 +42,7 @@ kda_status prefill_plain(const void* q, const void* k, const void* v,
   a.cu_seqlens = cu_seqlens; a.init_state = init_state; a.o = o; a.final_state = final_state;
   a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.num_heads = num_heads; a.d = dk;
   a.bf16 = dtype == KDA_BF16; a.workspace = workspace;
-  a.state_indices = nullptr; a.pool_slots = 0; a.scalar_gate = scalar_gate;
+  a.state_indices = nullptr; a.pool_slots = 0; a.scalar_gate = scalar_gate; a.raw_qkb = raw;
   const hipError_t e = a.bf16 ? kda::launch_prefill_bf16(a, stream) : kda::launch_prefill_f32(a, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -51,7 +51,7 @@ kda_status prefill_plain(const void* q, const void* k, const void* v,
 kda_status decode_plain(const void* q, const void* k, const void* v, const float* log_alpha,
                            const void* beta, float* state, void* o, int32_t num_seqs,
                            int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
-                           hipStream_t stream, bool scalar_gate) {
+                           hipStream_t stream, bool scalar_gate, bool raw) {
   kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
   if (st != KDA_OK) return st;
   if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_SHAPE;
@@ -64,7 +64,7 @@ kda_status decode_plain(const void* q, const void* k, const void* v, const float
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.state = state; a.o = o;
   a.num_seqs = num_seqs; a.num_heads = num_heads; a.d = dk; a.bf16 = dtype == KDA_BF16;
-  a.state_indices = nullptr; a.pool_slots = 0; a.scalar_gate = scalar_gate;
+  a.state_indices = nullptr; a.pool_slots = 0; a.scalar_gate = scalar_gate; a.raw_qkb = raw;
   return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -105,7 +105,8 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
                               kda_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
   return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
-                       total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, false);
+                       total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, false,
+                       false);
 }
 
 kda_status kda_gdn_prefill_varlen(const void* q, const void* k, const void* v,
@@ -116,7 +117,20 @@ kda_status kda_gdn_prefill_varlen(const void* q, const void* k, const void* v,
                                   kda_dtype dtype, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
   return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
-                       total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, true);
+                       total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, true,
+                       false);
+}
+
+kda_status kda_prefill_varlen_raw(const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const void* beta_logit,
+                                  const int32_t* cu_seqlens, const float* init_state,
+                                  void* o, float* final_state, int32_t num_seqs,
+                                  int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                  kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  return prefill_plain(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state, o, final_state, num_seqs,
+                       total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, false,
+                       true);
 }
 
 kda_status kda_prefill_varlen_pooled(const void* q, const void* k, const void* v,
@@ -143,7 +157,7 @@ kda_status kda_prefill_varlen_pooled(const void* q, const void* k, const void* v
   a.final_state = state_pool;
   a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.num_heads = num_heads; a.d = dk;
   a.bf16 = dtype == KDA_BF16; a.workspace = workspace;
-  a.state_indices = state_indices; a.pool_slots = pool_slots; a.scalar_gate = false;
+  a.state_indices = state_indices; a.pool_slots = pool_slots; a.scalar_gate = false; a.raw_qkb = false;
   const hipError_t e = a.bf16 ? kda::launch_prefill_bf16(a, stream) : kda::launch_prefill_f32(a, stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -152,14 +166,24 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            const void* beta, float* state, void* o, int32_t num_seqs,
                            int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
                            hipStream_t stream) {
-  return decode_plain(q, k, v, log_alpha, beta, state, o, num_seqs, num_heads, dk, dv, dtype, stream, false);
+  return decode_plain(q, k, v, log_alpha, beta, state, o, num_seqs, num_heads, dk, dv, dtype, stream, false,
+                      false);
+}
+
+kda_status kda_decode_step_raw(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const void* beta_logit, float* state, void* o, int32_t num_seqs,
+                               int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                               hipStream_t stream) {
+  return decode_plain(q, k, v, log_alpha, beta_logit, state, o, num_seqs, num_heads, dk, dv, dtype, stream,
+                      false, true);
 }
 
 kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                                const void* beta, float* state, void* o, int32_t num_seqs,
                                int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
                                hipStream_t stream) {
-  return decode_plain(q, k, v, log_alpha, beta, state, o, num_seqs, num_heads, dk, dv, dtype, stream, true);
+  return decode_plain(q, k, v, log_alpha, beta, state, o, num_seqs, num_heads, dk, dv, dtype, stream, true,
+                      false);
 }
 
 kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -178,7 +202,7 @@ kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v, c
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.state = state_pool; a.o = o;
   a.num_seqs = num_seqs; a.num_heads = num_heads; a.d = dk; a.bf16 = dtype == KDA_BF16;
-  a.state_indices = state_indices; a.pool_slots = pool_slots; a.scalar_gate = false;
+  a.state_indices = state_indices; a.pool_slots = pool_slots; a.scalar_gate = false; a.raw_qkb = false;
   return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

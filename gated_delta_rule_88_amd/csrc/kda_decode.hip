@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, float* __restrict__ state,
     typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H,
-    int scalar_gate) {
+    int scalar_gate, int raw_qkb) {
   using In = typename P::In;
   constexpr int NK = D / 16;        // keys per lane
   constexpr int NC = NK / 4;        // float4 pieces per lane and row
@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   const int l16 = tid & 15;
 
   // token vectors for this lane's keys: c * 64 + 4 * l16 + {0..3}
-  float a[NK], kk[NK], aq[NK], ak[NK];
-  float kq_part = 0.f;
+  float a[NK], kk[NK], qq[NK], aq[NK], ak[NK];
+  float ksq = 0.f, qsq = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t base = tok * D + c * 64 + 4 * l16;
@@ -57,18 +57,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
                                  : *reinterpret_cast<const f32x4*>(log_alpha + base);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ai = __expf(la[e]);
-      const float ki = to_f32(k[base + e]);
-      const float qi = to_f32(q[base + e]);
-      a[4 * c + e] = ai;
-      kk[4 * c + e] = ki;
-      ak[4 * c + e] = ai * ki;
-      aq[4 * c + e] = ai * qi;
-      kq_part += ki * qi;
+      a[4 * c + e] = __expf(la[e]);
+      kk[4 * c + e] = to_f32(k[base + e]);
+      qq[4 * c + e] = to_f32(q[base + e]);
+      ksq += kk[4 * c + e] * kk[4 * c + e];
+      qsq += qq[4 * c + e] * qq[4 * c + e];
     }
   }
+  // raw inputs: unit q and k (each 16-lane row holds a whole token vector)
+  const float rk = raw_qkb ? inv_norm(row16_sum(ksq)) : 1.f;
+  const float rq = raw_qkb ? inv_norm(row16_sum(qsq)) : 1.f;
+  float kq_part = 0.f;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    kk[i] *= rk;
+    const float qi = qq[i] * rq;
+    ak[i] = a[i] * kk[i];
+    aq[i] = a[i] * qi;
+    kq_part += kk[i] * qi;
+  }
   const float kq = row16_sum(kq_part);
-  const float b = to_f32(beta[tok]);
+  const float b = raw_qkb ? sigmoid(to_f32(beta[tok])) : to_f32(beta[tok]);
 
   float* srow0 = state + (slot * H + tok % H) * D * D;
   f32x4 s[ROWS][NC];
@@ -115,7 +124,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
                      (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
                      (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads,
-                     (int)A.scalar_gate);
+                     (int)A.scalar_gate, (int)A.raw_qkb);
   return hipGetLastError();
 }
 

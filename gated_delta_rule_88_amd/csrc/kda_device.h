@@ -122,6 +122,12 @@ __device__ __forceinline__ void mma_xs(f32x4& acc, const typename P::Frag& a, co
   if constexpr (P::kSplit) mma(acc, a, b.lo);
 }
 
+// The input prologue of the raw-input calls: x / max(|x|, 1e-12) per
+// (token, head) vector, and beta = 1 / (1 + e^-logit).
+constexpr float kNormEps = 1e-12f;
+__device__ __forceinline__ float inv_norm(float sumsq) { return 1.f / fmaxf(sqrtf(sumsq), kNormEps); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));

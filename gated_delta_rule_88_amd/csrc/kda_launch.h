@@ -19,6 +19,7 @@ struct DecodeArgs {
   const int32_t* state_indices;   // NULL: sequence n uses state[n]
   int32_t pool_slots;
   bool scalar_gate;               // log_alpha holds one gate per (sequence, head)
+  bool raw_qkb;                   // q, k unnormalised and beta a logit (normalised in the kernel)
 };
 
 struct PrefillArgs {
@@ -37,6 +38,7 @@ struct PrefillArgs {
   const int32_t* state_indices;   // NULL: sequence n uses init_state[n] / final_state[n]
   int32_t pool_slots;
   bool scalar_gate;               // log_alpha holds one gate per (token, head)
+  bool raw_qkb;                   // q, k unnormalised and beta a logit (normalised in the kernel)
 };
 
 // Per-chunk factor record of the prefill (bytes) for each precision path,

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, const int32_t* __restrict__ cu, int N, int H,
-    unsigned char* __restrict__ ws, int scalar_gate) {
+    unsigned char* __restrict__ ws, int scalar_gate, int raw_qkb) {
   using In = typename P::In;
   using Frag = typename P::Frag;
   using Half = typename P::Half;
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
   __shared__ __align__(16) float sL[C][PL];               // Diag(beta) A (strictly lower)
   __shared__ float sEgm[D], sEcm[D], sGm[D], sGc[D], sBeta[C];
   __shared__ float sSeg[NTH / 64][D];
+  __shared__ float sNrm[2][C];                            // raw inputs: 1/|k|, 1/|q| per token
   __shared__ float sScr[4][16][17];
   In (*sQ)[PI] = reinterpret_cast<In (*)[PI]>(sQraw);
   float (*sT)[PL] = reinterpret_cast<float (*)[PL]>(sQraw);
@@ -135,8 +136,28 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
       *reinterpret_cast<uint4*>(&sK[r][cv * EV]) = kq;
       *reinterpret_cast<uint4*>(&sQ[r][cv * EV]) = qq;
     }
-    if (tid < C) sBeta[tid] = tid < len ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+    if (tid < C) {
+      const float b = tid < len ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+      sBeta[tid] = (raw_qkb && tid < len) ? sigmoid(b) : b;
+    }
     for (int idx = tid; idx < C * PL; idx += NTH) (&sL[0][0])[idx] = 0.f;
+  }
+  if (raw_qkb) {   // unit q and k rows, in place
+    __syncthreads();
+    if (tid < 2 * C) {
+      const int r = tid % C;
+      const In* row = tid < C ? &sK[r][0] : &sQ[r][0];
+      float ss = 0.f;
+      for (int i = 0; i < D; ++i) ss += to_f32(row[i]) * to_f32(row[i]);
+      sNrm[tid / C][r] = inv_norm(ss);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * D; idx += NTH) {
+      const int r = idx / D, i = idx % D;
+      sK[r][i] = from_f32<In>(to_f32(sK[r][i]) * sNrm[0][r]);
+      sQ[r][i] = from_f32<In>(to_f32(sQ[r][i]) * sNrm[1][r]);
+    }
+    __syncthreads();
   }
 
   // ---- phase 2: cumulative log decay and the anchored factor X -------------
@@ -609,7 +630,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_prep_kernel<P, D>), dim3((unsigned)slots, (unsigned)A.num_heads),
                        dim3(kPrepThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
                        A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads,
-                       (unsigned char*)A.workspace, (int)A.scalar_gate);
+                       (unsigned char*)A.workspace, (int)A.scalar_gate, (int)A.raw_qkb);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

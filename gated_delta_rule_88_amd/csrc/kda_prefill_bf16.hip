@@ -113,7 +113,7 @@ template <int D>
 __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
-    int N, int H, unsigned char* __restrict__ ws, int scalar_gate) {
+    int N, int H, unsigned char* __restrict__ ws, int scalar_gate, int raw_qkb) {
   using R = Rec<D>;
   using L = PrepLds<D>;
   constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
@@ -164,6 +164,29 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         }
       }
     if (valid) bt = (float)beta[(t0 + r) * H + h];
+  }
+  // raw inputs: unit q and k per token (the token's keys sit in lanes
+  // l16 + 16 g, g = 0..3) and beta from its logit
+  float rk = 1.f, rq = 1.f;
+  if (raw_qkb) {
+    float ksq = 0.f, qsq = 0.f;
+#pragma unroll
+    for (int p = 0; p < KB; ++p)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k1 = (float)kr[p][hh][e], q1 = (float)qr[p][hh][e];
+          ksq += k1 * k1;
+          qsq += q1 * q1;
+        }
+    ksq += __shfl_xor(ksq, 16);
+    ksq += __shfl_xor(ksq, 32);
+    qsq += __shfl_xor(qsq, 16);
+    qsq += __shfl_xor(qsq, 32);
+    rk = inv_norm(ksq);
+    rq = inv_norm(qsq);
+    if (r < len) bt = sigmoid(bt);
   }
 
   // ---- A: cumulative log decay over the tokens ---------------------------------
@@ -242,7 +265,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         const float dg = gr[p][hh][e] - gm;
         const float x = __expf(dg), ix = __expf(-dg);
         const float egm = egm4[e], ecm = ecm4[e];
-        const float kx = (float)kr[p][hh][e], qx = (float)qr[p][hh][e];
+        const float kx = (float)kr[p][hh][e] * rk, qx = (float)qr[p][hh][e] * rq;
         const float ka = kx * x, kb = kx * ix, qa = qx * x;
         kaF[p][m] = (In)ka;
         kbH[p][m] = (In)kb;
@@ -677,7 +700,8 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   if (A.total_tokens > 0) {
     hipLaunchKernelGGL((prep_kernel<D>), dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                        (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens,
-                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace, (int)A.scalar_gate);
+                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace, (int)A.scalar_gate,
+                       (int)A.raw_qkb);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -50,11 +50,12 @@ def load(path: str = LIB_PATH):
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
-    for name in ("kda_gdn_prefill_varlen",):
+    for name in ("kda_gdn_prefill_varlen", "kda_prefill_varlen_raw"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = lib.kda_prefill_varlen.argtypes
-    lib.kda_gdn_decode_step.restype = ctypes.c_int
-    lib.kda_gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
+    for name in ("kda_gdn_decode_step", "kda_decode_step_raw"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = lib.kda_decode_step.argtypes
     lib.kda_prefill_varlen_pooled.restype = ctypes.c_int
     lib.kda_prefill_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                               i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
@@ -114,6 +115,14 @@ def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
                     want_final=want_final, workspace=workspace, scalar_gate=False)
 
 
+def kda_prefill_varlen_raw(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state=None, *,
+                           o=None, final_state=None, want_final: bool = True, workspace=None):
+    """As :func:`kda_prefill_varlen` with unnormalised q, k (made unit length
+    per token and head inside the kernels) and beta given as a logit."""
+    return _prefill(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state, o=o, final_state=final_state,
+                    want_final=want_final, workspace=workspace, scalar_gate=False, raw=True)
+
+
 def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
                        o=None, final_state=None, want_final: bool = True, workspace=None):
     """Gated DeltaNet prefill: as :func:`kda_prefill_varlen` with one gate per
@@ -123,7 +132,7 @@ def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
 
 
 def _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, *, o, final_state, want_final,
-             workspace, scalar_gate):
+             workspace, scalar_gate, raw=False):
     """Chunked prefill over packed sequences; returns ``(o, final_state)``.
 
     q, k ``[T,H,dk]``; v ``[T,H,dv]`` (bf16 or fp32, one dtype); log_alpha
@@ -155,7 +164,8 @@ def _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, *, o, final_state
     need = int(lib.kda_prefill_workspace_size(N, T, H, dk, dv, code))
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    name = "kda_gdn_prefill_varlen" if scalar_gate else "kda_prefill_varlen"
+    name = ("kda_gdn_prefill_varlen" if scalar_gate else
+            "kda_prefill_varlen_raw" if raw else "kda_prefill_varlen")
     st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                             _ptr(cu_seqlens), _ptr(init_state), _ptr(o), _ptr(final_state),
                             N, T, H, dk, dv, code, _ptr(workspace), workspace.numel(),
@@ -171,13 +181,18 @@ def kda_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
     return _decode(q, k, v, log_alpha, beta, state, o=o, scalar_gate=False)
 
 
+def kda_decode_step_raw(q, k, v, log_alpha, beta_logit, state, *, o=None):
+    """As :func:`kda_decode_step` with unnormalised q, k and beta as a logit."""
+    return _decode(q, k, v, log_alpha, beta_logit, state, o=o, scalar_gate=False, raw=True)
+
+
 def gdn_decode_step(q, k, v, log_alpha, beta, state, *, o=None):
     """Gated DeltaNet decode step: ``log_alpha [N,H]`` fp32, one gate per
     (sequence, head); otherwise as :func:`kda_decode_step`."""
     return _decode(q, k, v, log_alpha, beta, state, o=o, scalar_gate=True)
 
 
-def _decode(q, k, v, log_alpha, beta, state, *, o, scalar_gate):
+def _decode(q, k, v, log_alpha, beta, state, *, o, scalar_gate, raw=False):
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -192,7 +207,7 @@ def _decode(q, k, v, log_alpha, beta, state, *, o, scalar_gate):
     if o is None:
         o = torch.empty((N, H, dv), device=q.device, dtype=dt)
     _check(o, "o", (N, H, dv), dt)
-    name = "kda_gdn_decode_step" if scalar_gate else "kda_decode_step"
+    name = "kda_gdn_decode_step" if scalar_gate else "kda_decode_step_raw" if raw else "kda_decode_step"
     st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                             _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(q.device))
     if st != 0:

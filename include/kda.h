@@ -181,6 +181,34 @@ kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v,
                                hipStream_t stream);
 
 /*
+ * Raw-input forms of the KDA calls: the kernels apply the layer's input
+ * prologue themselves -- q and k are made unit length per (token, head),
+ * x / max(|x|_2, 1e-12) in fp32, and beta is given as a logit and taken
+ * through the sigmoid (the "Kimi Linear Guide" page, "End-to-End
+ * Implementation": keys and queries normalised, the write strength squashed
+ * to (0, 1); the "Kimi Delta Attention" page §02 assumes normalised keys).
+ * Arguments, layouts and errors as for kda_prefill_varlen and
+ * kda_decode_step, with beta_logit in place of beta.
+ */
+kda_status kda_prefill_varlen_raw(const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const void* beta_logit,
+                                  const int32_t* cu_seqlens,
+                                  const float* init_state,
+                                  void* o, float* final_state,
+                                  int32_t num_seqs, int64_t total_tokens,
+                                  int32_t num_heads, int32_t dk, int32_t dv,
+                                  kda_dtype dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+kda_status kda_decode_step_raw(const void* q, const void* k, const void* v,
+                               const float* log_alpha, const void* beta_logit,
+                               float* state, void* o,
+                               int32_t num_seqs, int32_t num_heads,
+                               int32_t dk, int32_t dv, kda_dtype dtype,
+                               hipStream_t stream);
+
+/*
  * State-pool forms of the two calls, for a serving engine that keeps every
  * live sequence's recurrent state in one caller-owned pool and checkpoints
  * prefixes ("Kimi Delta Attention" §07: the fixed-size state is the whole

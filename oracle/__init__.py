@@ -13,6 +13,11 @@ compiles it with gcc on first use, marshals arrays and exposes two calls:
 * :func:`decode_step` -- one token per (sequence, head): exactly one loop
   iteration of the same recurrence (the "fused recurrent" decode mode of §06).
 
+:func:`prefill_raw` and :func:`decode_step_raw` apply the layer's input
+prologue first (q, k made unit length per token and head with the 1e-12
+floor of torch's ``normalize``, beta = sigmoid(logit)), in fp64, then run the
+same recurrence.
+
 :func:`prefill_scalar_gate` and :func:`decode_step_scalar_gate` take one gate
 per (token, head) -- the scalar-gated delta rule (Gated DeltaNet) that §02-§03
 refine into KDA -- and run the same recurrence with that gate repeated over
@@ -215,3 +220,23 @@ def decode_step_scalar_gate(q, k, v, log_alpha, beta, state, **kw):
     """:func:`decode_step` with ``log_alpha [N,H]``."""
     dk = _typed(q)[0].shape[-1]
     return decode_step(q, k, v, _repeat_gate(log_alpha, dk), beta, state, **kw)
+
+
+def _unit_rows(x):
+    a = _f64(x)
+    return a / np.maximum(np.sqrt(np.sum(a * a, axis=-1, keepdims=True)), 1e-12)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-_f64(x)))
+
+
+def prefill_raw(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state=None, **kw):
+    """:func:`prefill` on unnormalised q, k and beta logits."""
+    return prefill(_unit_rows(q), _unit_rows(k), _f64(v), log_alpha, _sigmoid(beta_logit), cu_seqlens,
+                   init_state, **kw)
+
+
+def decode_step_raw(q, k, v, log_alpha, beta_logit, state, **kw):
+    """:func:`decode_step` on unnormalised q, k and beta logits."""
+    return decode_step(_unit_rows(q), _unit_rows(k), _f64(v), log_alpha, _sigmoid(beta_logit), state, **kw)

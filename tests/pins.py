@@ -320,6 +320,30 @@ def check_scalar_gate_exact(lib, seed=13):
         assert _rel(fin[0, 0], f(S).T) < 1e-12, ("scalar gate state vs exact", dk, dv)
 
 
+# --------------------------------------------------------------------------
+# 13. Raw-input prologue: outputs do not depend on the length of q and k
+#     (each is made unit length), and with unit q, k and beta = sigmoid(x)
+#     the raw form is the plain recurrence
+# --------------------------------------------------------------------------
+def check_raw_prologue(lib, seed=14):
+    rng = np.random.default_rng(seed)
+    T, H, dk, dv = 9, 2, 5, 3
+    q, k, v, la, beta = _rand_inputs(rng, T, H, dk, dv)      # unit q, k
+    logit = np.log(beta / (1.0 - beta))
+    s0 = rng.standard_normal((1, H, dv, dk))
+    o_plain, f_plain = _run(lib, q, k, v, la, beta, [0, T], s0)
+    scale_q = rng.uniform(0.2, 5.0, (T, H, 1))
+    scale_k = rng.uniform(0.2, 5.0, (T, H, 1))
+    o_raw, f_raw = oracle.prefill_raw(q * scale_q, k * scale_k, v, la, logit, np.array([0, T]), s0, lib=lib)
+    assert _rel(o_raw, o_plain) < 1e-12 and _rel(f_raw, f_plain) < 1e-12, "raw prologue"
+    # a zero vector stays zero (the 1e-12 floor), which makes that token's write vanish
+    kz = k.copy()
+    kz[3] = 0.0
+    o_z, _ = oracle.prefill_raw(q, kz, v, la, logit, np.array([0, T]), s0, lib=lib)
+    o_ref, _ = _run(lib, q, kz, v, la, beta, [0, T], s0)
+    assert _rel(o_z, o_ref) < 1e-12, "zero key"
+
+
 ALL_CHECKS = [
     check_exact_bruteforce,
     check_golden_worked_example,
@@ -333,4 +357,5 @@ ALL_CHECKS = [
     check_column_permutation,
     check_continuation_and_packing,
     check_scalar_gate_exact,
+    check_raw_prologue,
 ]
