@@ -294,6 +294,18 @@ def main():
     torch.cuda.synchronize()
     pool_ms = [e[0].elapsed_time(e[1]) for e in evp]
 
+    # the decode workload as a sequence: 512 consecutive steps timed end to
+    # end (inputs cycle through the resident steps), three repeats
+    seq_steps, seq_ms = 512, []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(seq_steps):
+            decode(s)
+        e1.record()
+        torch.cuda.synchronize()
+        seq_ms.append(e0.elapsed_time(e1) / seq_steps)
+
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     pre_avg = sum(pre_ms) / K
@@ -338,8 +350,14 @@ def main():
                               "dv": dwl.dv,
                               "state_MB": round(dwl.num_seqs * dwl.heads * dwl.dk * dwl.dv * 4 / 1e6, 1)}},
         "prefill": {"ms": round(pre_avg, 5), "ms_min": round(min(pre_ms), 5),
+                    "ms_median": round(sorted(pre_ms)[K // 2], 5),
                     "tokens_per_s": round(T / (pre_avg * 1e-3), 1), "roofline": roof_pre},
         "decode": {"ms": round(dec_avg, 5), "ms_min": round(min(dec_ms), 5),
+                   "ms_median": round(sorted(dec_ms)[K // 2], 5),
+                   "sequence_512": {"ms_per_step": round(min(seq_ms), 5),
+                                    "GB_s": round(dbytes / (min(seq_ms) * 1e-3) / 1e9, 1),
+                                    "frac_hbm": round(dbytes / (min(seq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                    "repeats": 3},
                    "value": round(dec_gbps, 1), "unit": "GB/s",
                    "tokens_per_s": round(dwl.num_seqs / (dec_avg * 1e-3), 1), "roofline": roof_dec},
         "gdn_prefill": {"ms": round(sum(gdn_ms) / K, 5), "ms_min": round(min(gdn_ms), 5),

@@ -28,13 +28,14 @@ namespace kda {
 
 constexpr int kDecodeThreads = 1024;
 
-template <class P, int D>
+// SCALAR: one gate per (sequence, head); RAW: q, k unnormalised and beta a
+// logit.  Compile-time, so the plain KDA step carries neither.
+template <class P, int D, bool SCALAR, bool RAW>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
     const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
     const typename P::In* __restrict__ beta, float* __restrict__ state,
-    typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H,
-    int scalar_gate, int raw_qkb) {
+    typename P::In* __restrict__ o, const int32_t* __restrict__ sidx, int pool_slots, int H) {
   using In = typename P::In;
   constexpr int NK = D / 16;        // keys per lane
   constexpr int NC = NK / 4;        // float4 pieces per lane and row
@@ -53,8 +54,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t base = tok * D + c * 64 + 4 * l16;
-    const f32x4 la = scalar_gate ? f32x4{log_alpha[tok], log_alpha[tok], log_alpha[tok], log_alpha[tok]}
-                                 : *reinterpret_cast<const f32x4*>(log_alpha + base);
+    f32x4 la;
+    if constexpr (SCALAR) la = f32x4{log_alpha[tok], log_alpha[tok], log_alpha[tok], log_alpha[tok]};
+    else la = *reinterpret_cast<const f32x4*>(log_alpha + base);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       a[4 * c + e] = __expf(la[e]);
@@ -65,8 +67,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     }
   }
   // raw inputs: unit q and k (each 16-lane row holds a whole token vector)
-  const float rk = raw_qkb ? inv_norm(row16_sum(ksq)) : 1.f;
-  const float rq = raw_qkb ? inv_norm(row16_sum(qsq)) : 1.f;
+  float rk = 1.f, rq = 1.f;
+  if constexpr (RAW) {
+    rk = inv_norm(row16_sum(ksq));
+    rq = inv_norm(row16_sum(qsq));
+  }
   float kq_part = 0.f;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
@@ -77,7 +82,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     kq_part += kk[i] * qi;
   }
   const float kq = row16_sum(kq_part);
-  const float b = raw_qkb ? sigmoid(to_f32(beta[tok])) : to_f32(beta[tok]);
+  float b = to_f32(beta[tok]);
+  if constexpr (RAW) b = sigmoid(b);
 
   float* srow0 = state + (slot * H + tok % H) * D * D;
   f32x4 s[ROWS][NC];
@@ -117,15 +123,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
   if (l16 < ROWS) o[tok * D + grp * ROWS + l16] = from_f32<In>(my_o);
 }
 
-template <class P, int D>
-static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+template <class P, int D, bool SCALAR, bool RAW>
+static hipError_t launch_decode_v(const DecodeArgs& A, hipStream_t stream) {
   using In = typename P::In;
   const unsigned blocks = (unsigned)((int64_t)A.num_seqs * A.num_heads);
-  hipLaunchKernelGGL((decode_step_kernel<P, D>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
+  hipLaunchKernelGGL((decode_step_kernel<P, D, SCALAR, RAW>), dim3(blocks), dim3(kDecodeThreads), 0, stream,
                      (const In*)A.q, (const In*)A.k, (const In*)A.v, A.log_alpha,
-                     (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads,
-                     (int)A.scalar_gate, (int)A.raw_qkb);
+                     (const In*)A.beta, A.state, (In*)A.o, A.state_indices, A.pool_slots, A.num_heads);
   return hipGetLastError();
+}
+
+template <class P, int D>
+static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+  if (A.scalar_gate) return launch_decode_v<P, D, true, false>(A, stream);
+  if (A.raw_qkb) return launch_decode_v<P, D, false, true>(A, stream);
+  return launch_decode_v<P, D, false, false>(A, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& A, hipStream_t stream) {
