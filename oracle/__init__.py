@@ -18,6 +18,10 @@ prologue first (q, k made unit length per token and head with the 1e-12
 floor of torch's ``normalize``, beta = sigmoid(logit)), in fp64, then run the
 same recurrence.
 
+:func:`prefill_grad` returns the gradients of a prefill (reverse mode of the
+same token recurrence, ``kda_oracle_grad.c``) for given output and
+final-state gradients.
+
 :func:`prefill_scalar_gate` and :func:`decode_step_scalar_gate` take one gate
 per (token, head) -- the scalar-gated delta rule (Gated DeltaNet) that §02-§03
 refine into KDA -- and run the same recurrence with that gate repeated over
@@ -37,6 +41,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
+_GRAD_SRC = os.path.join(_HERE, "kda_oracle_grad.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD_DIR, "libkda_oracle.so")
 
@@ -47,14 +52,16 @@ _lock = threading.Lock()
 _lib = None
 
 
-def build(src: str = _SRC, out: str = _LIB_PATH, force: bool = False) -> str:
-    """Compile the oracle with gcc (fp64, -O2, no fast-math) into ``out``."""
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+def build(src: str = _SRC, out: str = _LIB_PATH, force: bool = False, grad_src: str = _GRAD_SRC) -> str:
+    """Compile the oracle (forward ``src`` and gradient ``grad_src``) with gcc
+    (fp64, -O2, no fast-math) into ``out``."""
+    if (not force and os.path.exists(out)
+            and os.path.getmtime(out) >= max(os.path.getmtime(src), os.path.getmtime(grad_src))):
         return out
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", src, grad_src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -78,6 +85,15 @@ def load(path: str | None = None):
             vp, i64,                 # out_rows n_out_rows
             vp,                      # final_state
             i32, i32, i32, i32, i32  # H dk dv mode nthreads
+        ]
+        lib.kda_oracle_prefill_grad.restype = i32
+        lib.kda_oracle_prefill_grad.argtypes = [
+            vp, vp, vp, vp, vp,      # q k v log_alpha beta
+            i32, i32,                # in_type la_type
+            vp, i32,                 # cu_seqlens num_seqs
+            vp, vp, vp,              # init_state d_o d_final
+            vp, vp, vp, vp, vp, vp,  # dq dk dv dlog_alpha dbeta d_init
+            i32, i32, i32, i32       # H dk dv nthreads
         ]
         if path is None:
             _lib = lib
@@ -188,6 +204,54 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_prefill failed with code {rc}")
     return o, fin
+
+
+def prefill_grad(q, k, v, log_alpha, beta, cu_seqlens, init_state, d_o, d_final=None, *,
+                 nthreads: int | None = None, lib=None):
+    """Gradients of ``L = sum(d_o * o) + sum(d_final * final_state)`` for
+    :func:`prefill` on the same inputs.
+
+    ``d_o`` is ``[T,H,dv]``; ``d_final`` ``[N,H,dv,dk]`` or None (zero).
+    Returns a dict of float64 arrays: ``q``, ``k`` ``[T,H,dk]``, ``v``
+    ``[T,H,dv]``, ``log_alpha`` ``[T,H,dk]``, ``beta`` ``[T,H]`` and
+    ``init_state`` ``[N,H,dv,dk]``.
+    """
+    lib = lib or load()
+    qa, tq = _typed(q)
+    ka, tk = _typed(k)
+    va, tv = _typed(v)
+    ba, tb = _typed(beta)
+    if not (tq == tk == tv == tb):
+        raise TypeError("q, k, v and beta must share one dtype")
+    la, tla = _typed(log_alpha, allow=(F32, F64))
+    T, H, dk = qa.shape
+    dv = va.shape[-1]
+    if ka.shape != (T, H, dk) or la.shape != (T, H, dk) or va.shape != (T, H, dv) or ba.shape != (T, H):
+        raise ValueError("inconsistent input shapes")
+    cu = np.ascontiguousarray(np.asarray(
+        cu_seqlens.cpu().numpy() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if N < 0 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    s0 = _f64(init_state)
+    if s0 is not None and s0.shape != (N, H, dv, dk):
+        raise ValueError("init_state must be [N,H,dv,dk]")
+    go = _f64(d_o)
+    if go.shape != (T, H, dv):
+        raise ValueError("d_o must be [T,H,dv]")
+    gf = _f64(d_final)
+    if gf is not None and gf.shape != (N, H, dv, dk):
+        raise ValueError("d_final must be [N,H,dv,dk]")
+    out = {"q": np.zeros((T, H, dk)), "k": np.zeros((T, H, dk)), "v": np.zeros((T, H, dv)),
+           "log_alpha": np.zeros((T, H, dk)), "beta": np.zeros((T, H)),
+           "init_state": np.zeros((N, H, dv, dk))}
+    rc = lib.kda_oracle_prefill_grad(
+        _ptr(qa), _ptr(ka), _ptr(va), _ptr(la), _ptr(ba), tq, tla, _ptr(cu), N, _ptr(s0), _ptr(go),
+        _ptr(gf), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["log_alpha"]),
+        _ptr(out["beta"]), _ptr(out["init_state"]), H, dk, dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill_grad failed with code {rc}")
+    return out
 
 
 def decode_step(q, k, v, log_alpha, beta, state, *, nthreads: int | None = None, lib=None):
