@@ -12,10 +12,13 @@ Prints one JSON line:
   ms_per_step  wall time of one whole step (prefill + decode step)
   decode       decode state GB/s and tokens/s from HIP events around each step
   roofline     the call with the larger share of the step, against its bound
+  backward     kda_prefill_backward on the 8K workload (gradients of every
+               input for seeded upstream gradients), against the fp32 MFMA peak
   cpu_baseline the fp64 oracle on the host cores, same prefill workload
 
 Other modes:
-  --part prefill|decode|copy   run one leg only (for profiler runs); "copy"
+  --part prefill|decode|backward|copy
+                               run one leg only (for profiler runs); "copy"
                                is a plain 1 GiB device copy used to calibrate
                                the memory counters
   --traffic [OUTDIR]           run the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
@@ -41,14 +44,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_prefill_8k_decode_256.json")
 COPY_BYTES = 1 << 30
 
 
+# the device code of the kernels whose memory counters the traffic record holds
+TRAFFIC_SOURCES = ("kda_prefill_bf16.hip", "kda_decode.hip", "kda_device.h", "kda_prefill_common.h")
+
+
 def source_digest() -> str:
-    """sha256 of the HIP sources, to tell whether stored counters still apply."""
+    """sha256 of the sources of the kernels the traffic record covers, to tell
+    whether its counters still apply."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_88_amd", "csrc", "*"))):
+    for p in sorted(os.path.join(ROOT, "gated_delta_rule_88_amd", "csrc", f) for f in TRAFFIC_SOURCES):
         with open(p, "rb") as fh:
             h.update(os.path.basename(p).encode())
             h.update(fh.read())
@@ -62,6 +71,18 @@ def prefill_algorithmic(T, H, d, n_seqs, init, final):
     state = d * d * 4 * n_seqs * H * ((1 if init else 0) + (1 if final else 0))
     flops_per_tok = 2 * (5 * 64 * d + 3 * d * d)
     return T * H * per_tok + state, T * H * flops_per_tok
+
+
+def backward_algorithmic(T, H, d, n_seqs, C=64):
+    """Bytes and MFMA FLOPs of one backward call on full chunks.  Reads q, k,
+    v, grad_o (bf16), log_alpha (fp32), beta (bf16); writes fp32 gradients of
+    q, k, v, log_alpha, beta; reads dL/dS_T and writes dL/dS_0 (fp32).  FLOPs
+    are the dense products of the chunked form: 28 C^2 d + 16 C d^2 + 4 C^3
+    per (chunk, head)."""
+    per_tok = 3 * d * 2 + d * 4 + 2 + d * 2 + 4 * d * 4 + 4
+    state = 2 * d * d * 4 * n_seqs * H
+    flops_chunk = 28 * C * C * d + 16 * C * d * d + 4 * C ** 3
+    return T * H * per_tok + state, (T // C) * H * flops_chunk
 
 
 def gdn_prefill_algorithmic(T, H, d, n_seqs, final):
@@ -173,13 +194,26 @@ def run_traffic(outdir):
 
 
 # ---------------------------------------------------------------------------
+def backward_report(ms, T, H, D):
+    bbytes, bflops = backward_algorithmic(T, H, D, 1)
+    avg = sum(ms) / len(ms)
+    tf = bflops / (avg * 1e-3) / 1e12
+    return {"ms": round(avg, 5), "ms_min": round(min(ms), 5), "calls": len(ms),
+            "tokens_per_s": round(T / (avg * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                         "hbm_frac": round(bbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "launch": "kda_prefill_backward: bwd_prep, bwd_fwd, bwd_dstate, bwd_grad (fp32 MFMA)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "prefill", "decode", "copy"), default="all")
+    ap.add_argument("--part", choices=("all", "prefill", "decode", "backward", "copy"), default="all")
     ap.add_argument("--traffic", metavar="OUTDIR", nargs="?", const=os.path.join(ROOT, "gpurun_out", "traffic"))
     args = ap.parse_args()
     if args.gpus != 1:
@@ -239,6 +273,30 @@ def main():
         s %= n_dec
         kda.kda_decode_step_pooled(Dd["q"][s], Dd["k"][s], Dd["v"][s], Dd["log_alpha"][s], Dd["beta"][s],
                                    sidx, pool, o=od)
+
+    # backward of the same prefill for seeded upstream gradients
+    g_up = torch.Generator(device=dev).manual_seed(7)
+    grad_o = torch.randn((T, H, D), device=dev, generator=g_up).to(torch.bfloat16)
+    grad_fin = torch.randn((1, H, D, D), device=dev, generator=g_up)
+    f32 = dict(device=dev, dtype=torch.float32)
+    grads = {"q": torch.empty((T, H, D), **f32), "k": torch.empty((T, H, D), **f32),
+             "v": torch.empty((T, H, D), **f32), "log_alpha": torch.empty((T, H, D), **f32),
+             "beta": torch.empty((T, H), **f32), "init_state": torch.empty((1, H, D, D), **f32)}
+    ws_b = None
+
+    def backward():
+        nonlocal ws_b
+        if ws_b is None:
+            ws_b = torch.empty(kda.backward_workspace_size(1, T, H, D, D, torch.bfloat16), device=dev,
+                               dtype=torch.uint8)
+        kda.kda_prefill_backward(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["cu_seqlens"], None,
+                                 grad_o, grad_fin, grads=grads, workspace=ws_b)
+
+    if args.part == "backward":
+        for s in range(args.warmup + args.steps):
+            backward()
+        torch.cuda.synchronize()
+        return
 
     if args.part in ("prefill", "decode"):
         for s in range(args.warmup + args.steps):
@@ -306,6 +364,19 @@ def main():
         torch.cuda.synchronize()
         seq_ms.append(e0.elapsed_time(e1) / seq_steps)
 
+    # backward, timed on its own (fewer repeats: it is the longest call)
+    Kb = max(3, K // 4)
+    for _ in range(min(args.warmup, 2)):
+        backward()
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(Kb)]
+    for s in range(Kb):
+        evb[s][0].record()
+        backward()
+        evb[s][1].record()
+    torch.cuda.synchronize()
+    bwd_ms = [e[0].elapsed_time(e[1]) for e in evb]
+    ws_b = None
+
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     pre_avg = sum(pre_ms) / K
@@ -370,6 +441,7 @@ def main():
                           "value": round(dbytes / (sum(pool_ms) / K * 1e-3) / 1e9, 1), "unit": "GB/s",
                           "pool_slots": 2 * dwl.num_seqs,
                           "launch": "kda_decode_step_pooled: decode_step_kernel with a slot map"},
+        "backward": backward_report(bwd_ms, T, H, D),
         "roofline": dominant,
     }
     if not args.no_cpu_baseline:

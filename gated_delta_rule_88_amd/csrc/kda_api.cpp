@@ -206,4 +206,43 @@ kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v, c
   return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_prefill_backward_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                           int32_t dk, int32_t dv, kda_dtype dtype) {
+  if (check_common(num_seqs, num_heads, dk, dv, dtype) != KDA_OK) return 0;
+  if (total_tokens < 0 || total_tokens > INT32_MAX) return 0;
+  const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
+  return (size_t)slots * (size_t)num_heads * kda::backward_block_bytes(dk);
+}
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                                const void* beta, const int32_t* cu_seqlens, const float* init_state,
+                                const void* grad_o, const float* grad_final_state, float* grad_q,
+                                float* grad_k, float* grad_v, float* grad_log_alpha, float* grad_beta,
+                                float* grad_init_state, int32_t num_seqs, int64_t total_tokens,
+                                int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !grad_o || !grad_q || !grad_k ||
+                           !grad_v || !grad_log_alpha || !grad_beta))
+    return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, init_state, grad_o, grad_final_state, grad_q,
+                        grad_k, grad_v, grad_log_alpha, grad_beta, grad_init_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const size_t need = kda_prefill_backward_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype);
+  if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.cu_seqlens = cu_seqlens;
+  a.init_state = init_state; a.grad_o = grad_o; a.grad_final_state = grad_final_state;
+  a.grad_q = grad_q; a.grad_k = grad_k; a.grad_v = grad_v; a.grad_log_alpha = grad_log_alpha;
+  a.grad_beta = grad_beta; a.grad_init_state = grad_init_state;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.num_heads = num_heads; a.d = dk;
+  a.bf16 = dtype == KDA_BF16; a.workspace = workspace;
+  return kda::launch_backward(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

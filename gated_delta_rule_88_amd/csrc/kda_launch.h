@@ -41,6 +41,23 @@ struct PrefillArgs {
   bool raw_qkb;                   // q, k unnormalised and beta a logit (normalised in the kernel)
 };
 
+struct BackwardArgs {
+  const void *q, *k, *v;
+  const float* log_alpha;
+  const void* beta;
+  const int32_t* cu_seqlens;
+  const float* init_state;        // NULL: zero initial states
+  const void* grad_o;             // dL/do, in the input type
+  const float* grad_final_state;  // NULL: zero
+  float *grad_q, *grad_k, *grad_v, *grad_log_alpha, *grad_beta;
+  float* grad_init_state;         // NULL: not written
+  int32_t num_seqs;
+  int64_t total_tokens;
+  int32_t num_heads, d;
+  bool bf16;
+  void* workspace;
+};
+
 // Per-chunk factor record of the prefill (bytes) for each precision path,
 // and the number of chunk slots reserved for (num_seqs, total_tokens).
 size_t prefill_record_bytes_f32(int d);
@@ -50,5 +67,9 @@ int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+
+// Backward: workspace bytes per (chunk slot, head) and the launcher.
+size_t backward_block_bytes(int d);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace kda

@@ -62,6 +62,13 @@ def load(path: str = LIB_PATH):
     lib.kda_decode_step_pooled.restype = ctypes.c_int
     lib.kda_decode_step_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                            ctypes.c_int, vp]
+    lib.kda_prefill_backward_workspace_size.restype = sz
+    lib.kda_prefill_backward_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill_backward.restype = ctypes.c_int
+    lib.kda_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp,          # q k v log_alpha beta cu init
+                                         vp, vp,                              # grad_o grad_final_state
+                                         vp, vp, vp, vp, vp, vp,              # grad_q k v log_alpha beta init
+                                         i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -277,3 +284,61 @@ def kda_decode_step_pooled(q, k, v, log_alpha, beta, state_indices, state_pool, 
     if st != 0:
         raise KdaError(st, "kda_decode_step_pooled")
     return o
+
+
+def backward_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                            dtype: torch.dtype) -> int:
+    """Bytes of workspace :func:`kda_prefill_backward` needs."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_backward_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def kda_prefill_backward(q, k, v, log_alpha, beta, cu_seqlens, init_state, grad_o, grad_final_state=None, *,
+                         want_grad_init=True, grads=None, workspace=None):
+    """Gradients of the varlen prefill for upstream ``grad_o [T,H,dv]`` (input
+    dtype) and ``grad_final_state [N,H,dv,dk]`` fp32 (or None = zero).
+
+    Returns a dict of fp32 tensors: ``q``, ``k`` ``[T,H,dk]``, ``v``
+    ``[T,H,dv]``, ``log_alpha`` ``[T,H,dk]``, ``beta`` ``[T,H]`` and
+    ``init_state`` ``[N,H,dv,dk]`` (None unless ``want_grad_init``).
+    ``grads`` may supply that dict's tensors to write into.
+    """
+    lib = load()
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", (T, H, dk), dt)
+    _check(k, "k", (T, H, dk), dt)
+    _check(v, "v", (T, H, dv), dt)
+    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32)
+    _check(beta, "beta", (T, H), dt)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    _check(grad_o, "grad_o", (T, H, dv), dt)
+    if init_state is not None:
+        _check(init_state, "init_state", (N, H, dv, dk), torch.float32)
+    if grad_final_state is not None:
+        _check(grad_final_state, "grad_final_state", (N, H, dv, dk), torch.float32)
+    f32 = dict(device=q.device, dtype=torch.float32)
+    if grads is None:
+        grads = {"q": torch.empty((T, H, dk), **f32), "k": torch.empty((T, H, dk), **f32),
+                 "v": torch.empty((T, H, dv), **f32), "log_alpha": torch.empty((T, H, dk), **f32),
+                 "beta": torch.empty((T, H), **f32),
+                 "init_state": torch.empty((N, H, dv, dk), **f32) if want_grad_init else None}
+    for name, shape in (("q", (T, H, dk)), ("k", (T, H, dk)), ("v", (T, H, dv)), ("log_alpha", (T, H, dk)),
+                        ("beta", (T, H))):
+        _check(grads[name], "grad_" + name, shape, torch.float32)
+    if grads.get("init_state") is not None:
+        _check(grads["init_state"], "grad_init_state", (N, H, dv, dk), torch.float32)
+    need = int(lib.kda_prefill_backward_workspace_size(N, T, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    st = lib.kda_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens),
+                                  _ptr(init_state), _ptr(grad_o), _ptr(grad_final_state), _ptr(grads["q"]),
+                                  _ptr(grads["k"]), _ptr(grads["v"]), _ptr(grads["log_alpha"]),
+                                  _ptr(grads["beta"]), _ptr(grads.get("init_state")), N, T, H, dk, dv, code,
+                                  _ptr(workspace), workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise KdaError(st, "kda_prefill_backward")
+    return grads

@@ -252,6 +252,52 @@ kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v,
                                   int32_t dk, int32_t dv, kda_dtype dtype,
                                   hipStream_t stream);
 
+/*
+ * Backward pass of kda_prefill_varlen (training; "Kimi Delta Attention" §06
+ * names training as the other user of the chunk-parallel form).  For a loss
+ * L with upstream gradients grad_o = dL/do and grad_final_state = dL/dS_T it
+ * writes the gradients of L with respect to every input of the forward call
+ * on the same arguments.  The pages give no gradient; it is the reverse-mode
+ * derivative of the recurrence above, organised by chunks of 64 tokens: a
+ * forward pass re-derives every chunk's entering state, a reverse pass over
+ * the chunks carries dL/dS, and each chunk then assembles its tokens'
+ * gradients from its own factors.
+ *
+ *   q, k, v, log_alpha, beta, cu_seqlens, init_state, num_seqs, total_tokens,
+ *   num_heads, dk, dv, dtype : exactly as passed to kda_prefill_varlen
+ *                    (init_state may be NULL = zeros)
+ *   grad_o           [T, H, dv] in `dtype` (required when T > 0)
+ *   grad_final_state [N, H, dv, dk] fp32, or NULL (zero)
+ *   grad_q, grad_k   [T, H, dk] fp32        (required when T > 0)
+ *   grad_v           [T, H, dv] fp32        (required when T > 0)
+ *   grad_log_alpha   [T, H, dk] fp32        (required when T > 0)
+ *   grad_beta        [T, H]     fp32        (required when T > 0)
+ *   grad_init_state  [N, H, dv, dk] fp32, or NULL (not written); it may be
+ *                    the same buffer as grad_final_state, no other aliasing
+ *   workspace        >= kda_prefill_backward_workspace_size(...) bytes of
+ *                    device memory, contents irrelevant on entry (it holds
+ *                    every chunk's factors and both state passes, about
+ *                    0.96 MiB per (64-token chunk, head) at dk = 128)
+ * Gradients are fp32 whatever `dtype` is.  Zero-length sequences give
+ * grad_init_state = grad_final_state.  Errors as for kda_prefill_varlen.
+ */
+size_t kda_prefill_backward_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                           int32_t num_heads, int32_t dk, int32_t dv,
+                                           kda_dtype dtype);
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* log_alpha, const void* beta,
+                                const int32_t* cu_seqlens, const float* init_state,
+                                const void* grad_o, const float* grad_final_state,
+                                float* grad_q, float* grad_k, float* grad_v,
+                                float* grad_log_alpha, float* grad_beta,
+                                float* grad_init_state,
+                                int32_t num_seqs, int64_t total_tokens,
+                                int32_t num_heads, int32_t dk, int32_t dv,
+                                kda_dtype dtype,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,39 @@ def test_decode_pooled_rejects(lib, over, expect):
 
 def test_decode_pooled_zero_sequences_is_a_no_op(lib):
     assert decode_pooled(lib, N=0, q=None, idx=None, pool=None) == OK
+
+
+def test_backward_workspace_size(lib):
+    f = lib.kda_prefill_backward_workspace_size
+    # per (chunk slot, head): 24 fp32 [64 x d] matrices, one fp64 [64 x d], 9 fp32
+    # [64 x 64], two [d x d] state blocks and the beta, diag(dBq), e^gC vectors
+    block_128 = 4 * (26 * 64 * 128 + 9 * 64 * 64 + 2 * 128 * 128 + 2 * 64 + 128)
+    assert f(1, 8192, 32, 128, 128, BF16) == (8192 // 64 + 1 + 1) * 32 * block_128
+    assert f(1, 256, 1, 64, 64, F32) > 0
+    assert f(1, 100, 2, 96, 96, BF16) == 0
+    assert f(1, 100, 2, 128, 128, 7) == 0
+    assert f(1, -1, 2, 128, 128, BF16) == 0
+
+
+def backward(lib, **over):
+    args = dict(q=P, k=P, v=P, la=P, beta=P, cu=P, init=None, go=P, gfin=None, gq=P, gk=P, gv=P, gla=P,
+                gbeta=P, ginit=None, N=1, T=128, H=2, dk=128, dv=128, dtype=BF16, ws=P, wsb=1 << 40,
+                stream=None)
+    args.update(over)
+    return lib.kda_prefill_backward(args["q"], args["k"], args["v"], args["la"], args["beta"], args["cu"],
+                                    args["init"], args["go"], args["gfin"], args["gq"], args["gk"], args["gv"],
+                                    args["gla"], args["gbeta"], args["ginit"], args["N"], args["T"], args["H"],
+                                    args["dk"], args["dv"], args["dtype"], args["ws"], args["wsb"],
+                                    args["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=None), NULL), (dict(go=None), NULL), (dict(gq=None), NULL), (dict(gk=None), NULL),
+    (dict(gv=None), NULL), (dict(gla=None), NULL), (dict(gbeta=None), NULL), (dict(cu=None), NULL),
+    (dict(N=0), SHAPE), (dict(T=-1), SHAPE), (dict(T=1 << 31), SHAPE), (dict(H=0), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(dk=128, dv=64), UNSUP), (dict(dtype=4), DTYPE),
+    (dict(go=MIS), ALIGN), (dict(gfin=MIS), ALIGN), (dict(ginit=MIS), ALIGN), (dict(gbeta=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=4096), WS),
+])
+def test_backward_rejects(lib, over, expect):
+    assert backward(lib, **over) == expect

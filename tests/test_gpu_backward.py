@@ -1,0 +1,108 @@
+"""GPU parity of kda_prefill_backward (through the C ABI) against the fp64
+gradient oracle on the same seeded inputs and upstream gradients.
+
+Metric: the row-relative error of tests/parity.py, rows being (token, head)
+for dq, dk, dv, dlog_alpha, tokens for dbeta, and (sequence, head) blocks
+for the initial-state gradient; tolerances as for the forward.
+"""
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_88_amd import inputs, kda
+from tests.parity import TOL, row_rel_err, state_rel_err
+from tests.test_gpu_prefill import make_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAMES = ("q", "k", "v", "log_alpha", "beta")
+
+
+def upstream(d, seed, with_final=True):
+    """Seeded upstream gradients: dL/do in the input dtype, dL/dS_T fp32."""
+    g = torch.Generator().manual_seed(seed)
+    T, H, D = d["q"].shape
+    N = d["cu_seqlens"].shape[0] - 1
+    go = torch.randn((T, H, D), generator=g).to(d["q"].dtype)
+    gf = torch.randn((N, H, D, D), generator=g) if with_final else None
+    return go, gf
+
+
+def run_both(d, go, gf, want_init=True):
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    got = kda.kda_prefill_backward(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                                   dev["cu_seqlens"], dev["init_state"], go.to(DEV),
+                                   None if gf is None else gf.to(DEV), want_grad_init=want_init)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_grad(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"].long(),
+                              d["init_state"], go, gf)
+    return got, ref
+
+
+def errors(got, ref):
+    e = {n: row_rel_err(got[n], ref[n]) for n in NAMES}
+    if got.get("init_state") is not None:
+        e["init_state"] = state_rel_err(got["init_state"], ref["init_state"])
+    return e
+
+
+def check(d, go, gf, tol, label, want_init=True):
+    got, ref = run_both(d, go, gf, want_init)
+    e = errors(got, ref)
+    print(label + ": " + ", ".join(f"d{n} {x:.2e}" for n, x in e.items()) + f" (tol {tol:g})", flush=True)
+    assert all(x <= tol for x in e.values()), (label, e)
+    return got
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.float32, 128), (torch.bfloat16, 64),
+                                     (torch.bfloat16, 128)], ids=["f32-64", "f32-128", "bf16-64", "bf16-128"])
+def test_backward_ragged(dtype, D):
+    d = make_case([1, 63, 64, 65, 0, 200, 129], H=3, D=D, dtype=dtype, seed=410 + D)
+    go, gf = upstream(d, seed=411 + D)
+    check(d, go, gf, TOL[dtype], f"backward ragged {dtype} D={D}")
+
+
+def test_backward_zero_states_and_no_final_gradient():
+    """init_state NULL and grad_final_state NULL; the initial-state gradient
+    is still produced"""
+    d = make_case([130, 64, 7], H=2, D=128, dtype=torch.bfloat16, seed=420, init_std=0.0)
+    go, _ = upstream(d, seed=421, with_final=False)
+    check(d, go, None, TOL[torch.bfloat16], "backward zero init, no dS_T")
+
+
+def test_backward_strong_decay_f32():
+    """gates at the bottom of the supported range (log alpha near -2.5)"""
+    d = make_case([150, 70], H=2, D=64, dtype=torch.float32, seed=430, u_range=(0.5, 0.9))
+    go, gf = upstream(d, seed=431)
+    check(d, go, gf, TOL[torch.float32], "backward strong decay f32")
+
+
+def test_backward_only_empty_sequences():
+    """no tokens at all: the initial-state gradient is the final-state one"""
+    d = make_case([0, 0], H=2, D=64, dtype=torch.float32, seed=440)
+    go, gf = upstream(d, seed=441)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    got = kda.kda_prefill_backward(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                                   dev["cu_seqlens"], dev["init_state"], go.to(DEV), gf.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(got["init_state"].cpu(), gf)
+
+
+def test_backward_is_deterministic():
+    d = make_case([300, 45], H=2, D=128, dtype=torch.bfloat16, seed=450)
+    go, gf = upstream(d, seed=451)
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    args = (dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["cu_seqlens"], dev["init_state"],
+            go.to(DEV), gf.to(DEV))
+    a = kda.kda_prefill_backward(*args)
+    b = kda.kda_prefill_backward(*args)
+    torch.cuda.synchronize()
+    for n in NAMES + ("init_state",):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_8k_full():
+    """the 8K single-sequence prefill shape (H=32, d=128, bf16), every gradient"""
+    d = inputs.prefill_inputs(inputs.WORKLOADS["prefill_8k"])
+    go, gf = upstream(d, seed=461)
+    check(d, go, gf, TOL[torch.bfloat16], "backward prefill_8k")
