@@ -91,46 +91,59 @@ constexpr int kGemmLds = 32 * 80 + 32 * 144;   // floats, for N <= 128
 
 template <int N, class Epi>
 __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int Kd, float* lds, Epi epi) {
-  constexpr int LA = 80, LB = N + 16;
+  constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
   float* sA = lds;
   float* sB = lds + 32 * LA;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nt = 0; nt < N / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
+  // one 32-deep panel of A and B in registers: loaded one panel ahead, so
+  // the next panel's loads are in flight while this one is multiplied
+  f32x4 ra[2], rb[NBQ];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      ra[it] = A.cs == 1
+                   ? *reinterpret_cast<const f32x4*>(A.p + (int64_t)(idx & 63) * A.rs + k0 + 4 * (idx >> 6))
+                   : *reinterpret_cast<const f32x4*>(A.p + (int64_t)(k0 + (idx >> 4)) * A.cs + 4 * (idx & 15));
+    }
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      rb[it] = B.cs == 1
+                   ? *reinterpret_cast<const f32x4*>(B.p + (int64_t)(k0 + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                   : *reinterpret_cast<const f32x4*>(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
+    }
+  };
+  __syncthreads();   // operands written just before by other threads are visible
+  load(0);
   for (int k0 = 0; k0 < Kd; k0 += 32) {
-    if (A.cs == 1) {   // reduction index contiguous in memory
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int idx = tid + 256 * it, r = idx & 63, kq = idx >> 6;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(A.p + (int64_t)r * A.rs + k0 + 4 * kq);
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      if (A.cs == 1) {   // reduction index contiguous in memory
+        const int r = idx & 63, kq = idx >> 6;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sA[(4 * kq + i) * LA + r] = x[i];
-      }
-    } else {           // row index contiguous
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int idx = tid + 256 * it, rq = idx & 15, k = idx >> 4;
-        *reinterpret_cast<f32x4*>(sA + k * LA + 4 * rq) =
-            *reinterpret_cast<const f32x4*>(A.p + (int64_t)(k0 + k) * A.cs + 4 * rq);
+        for (int i = 0; i < 4; ++i) sA[(4 * kq + i) * LA + r] = ra[it][i];
+      } else {           // row index contiguous
+        *reinterpret_cast<f32x4*>(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
       }
     }
-    if (B.cs == 1) {   // column index contiguous
-      for (int idx = tid; idx < 8 * N; idx += 256) {
-        const int nq = idx % (N / 4), k = idx / (N / 4);
-        *reinterpret_cast<f32x4*>(sB + k * LB + 4 * nq) =
-            *reinterpret_cast<const f32x4*>(B.p + (int64_t)(k0 + k) * B.rs + 4 * nq);
-      }
-    } else {           // reduction index contiguous
-      for (int idx = tid; idx < 8 * N; idx += 256) {
-        const int n = idx % N, kq = idx / N;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(B.p + (int64_t)n * B.cs + k0 + 4 * kq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sB[(4 * kq + i) * LB + n] = x[i];
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      if (B.cs == 1) {   // column index contiguous
+        *reinterpret_cast<f32x4*>(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+      } else {           // reduction index contiguous
+        const int n = idx % N, kq = idx / N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sB[(4 * kq + i) * LB + n] = rb[it][i];
       }
     }
     __syncthreads();
+    if (k0 + 32 < Kd) load(k0 + 32);
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 4) {
       const float a = sA[(kk + g) * LA + 16 * w + l16];
@@ -144,6 +157,162 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) epi(16 * w + 4 * g + i, 16 * nt + l16, acc[nt][i]);
   __syncthreads();
+}
+
+// The same product with the accumulators returned to the caller (inlined, so
+// they stay in registers): acc (64 x N) = A1 B1 (+ A2 B2 when K2 > 0), lane
+// layout as above (rows 16 w + 4 g + i, columns 16 nt + l16).  Begins and
+// ends with a barrier.
+template <int N>
+__device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2, int K2,
+                                      float* lds, f32x4 (&acc)[N / 16]) {
+  constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
+  float* sA = lds;
+  float* sB = lds + 32 * LA;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ra[2], rb[NBQ];
+  bool a_kc = true, b_nc = true;   // layouts of the panel in the registers
+  auto load = [&](int k0) {
+    const bool first = k0 < K1;
+    const Mat A = first ? A1 : A2, B = first ? B1 : B2;
+    const int kk = first ? k0 : k0 - K1;
+    a_kc = A.cs == 1;
+    b_nc = B.cs == 1;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      ra[it] = a_kc ? *reinterpret_cast<const f32x4*>(A.p + (int64_t)(idx & 63) * A.rs + kk + 4 * (idx >> 6))
+                    : *reinterpret_cast<const f32x4*>(A.p + (int64_t)(kk + (idx >> 4)) * A.cs + 4 * (idx & 15));
+    }
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      rb[it] = b_nc ? *reinterpret_cast<const f32x4*>(B.p + (int64_t)(kk + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                    : *reinterpret_cast<const f32x4*>(B.p + (int64_t)(idx % N) * B.cs + kk + 4 * (idx / N));
+    }
+  };
+  __syncthreads();
+  load(0);
+  const int Kd = K1 + K2;
+  for (int k0 = 0; k0 < Kd; k0 += 32) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      if (a_kc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sA[(4 * (idx >> 6) + i) * LA + (idx & 63)] = ra[it][i];
+      } else {
+        *reinterpret_cast<f32x4*>(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      if (b_nc) {
+        *reinterpret_cast<f32x4*>(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sB[(4 * (idx / N) + i) * LB + idx % N] = rb[it][i];
+      }
+    }
+    __syncthreads();
+    if (k0 + 32 < Kd) load(k0 + 32);
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      const float a = sA[(kk + g) * LA + 16 * w + l16];
+#pragma unroll
+      for (int nt = 0; nt < N / 16; ++nt) acc[nt] = mfma4(a, sB[(kk + g) * LB + 16 * nt + l16], acc[nt]);
+    }
+    __syncthreads();
+  }
+}
+
+constexpr Mat kNoMat = {nullptr, 1, 1};
+
+// What the epilogue of a 64 x D product does with acc, the product (every
+// part optional; each array is row-major [C][D] in the workspace block):
+//   store = acc * store_scale;  out[(row) * out_rs + col] = beta_row * acc
+//   for rows < len (the value gradient, straight into the output);
+//   x  = (x_add ? x : 0) + s_row * acc * fx;
+//   dg = (g_add ? dg : 0) + g_sign * s_row * acc * fg   (fp64, exact products)
+// with s_row = beta_row when row_beta, else 1.  Each part loads everything it
+// needs before its first store, so a lane keeps its loads in flight.
+struct EpiD {
+  float* store = nullptr;
+  float store_scale = 1.f;
+  float* out = nullptr;
+  int64_t out_rs = 0;
+  int len = 0;
+  float* x = nullptr;
+  const float* fx = nullptr;
+  bool x_add = false;
+  double* dg = nullptr;
+  const float* fg = nullptr;
+  bool g_add = false;
+  float g_sign = 1.f;
+  bool row_beta = false;
+  const float* beta = nullptr;
+};
+
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2,
+                                                 int K2, float* lds, const EpiD e) {
+  constexpr int NT = D / 16;
+  f32x4 acc[NT];
+  wg_mm<D>(A1, B1, K1, A2, B2, K2, lds, acc);
+  const int w = threadIdx.x >> 6, g = (threadIdx.x & 63) >> 4, l16 = threadIdx.x & 15;
+  const int64_t lane = (int64_t)(16 * w + 4 * g) * D + l16;   // this lane's first element
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = e.row_beta ? e.beta[16 * w + 4 * g + i] : 1.f;
+  if (e.store) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.store[lane + i * D + 16 * nt] = e.store_scale * acc[nt][i];
+  }
+  if (e.out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * g + i;
+      const float b = e.beta[r];
+      if (r < e.len)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) e.out[r * e.out_rs + 16 * nt + l16] = b * acc[nt][i];
+    }
+  }
+  if (e.x) {
+    f32x4 f[NT], x[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[nt][i] = e.fx[lane + i * D + 16 * nt];
+        x[nt][i] = e.x_add ? e.x[lane + i * D + 16 * nt] : 0.f;
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e.x[lane + i * D + 16 * nt] = x[nt][i] + s[i] * acc[nt][i] * f[nt][i];
+  }
+  if (e.dg) {
+    f32x4 f[NT];
+    double d[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[nt][i] = e.fg[lane + i * D + 16 * nt];
+        d[nt][i] = e.g_add ? e.dg[lane + i * D + 16 * nt] : 0.0;
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        e.dg[lane + i * D + 16 * nt] = d[nt][i] + (double)(e.g_sign * s[i] * acc[nt][i]) * (double)f[nt][i];
+  }
 }
 
 template <class In>
@@ -172,6 +341,18 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
   float* B = ws + item * L::FLOATS;
   const int tid = threadIdx.x;
 
+  // the chunk's log decays, staged in LDS by the whole workgroup (rows past
+  // the chunk's end read as zero).  Every load in this kernel reads a row
+  // clamped into the chunk and selects zero afterwards, so that loads are
+  // never conditional and can all be in flight together.
+  float* sLa = lds;   // [C][D], overlaps the GEMM staging area (not yet in use)
+#pragma unroll
+  for (int it = 0; it < C * D / 4 / kThreads; ++it) {
+    const int idx = tid + kThreads * it, r = idx / (D / 4), cq = idx % (D / 4);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(log_alpha + ((t0 + min(r, len - 1)) * H + h) * D + 4 * cq);
+    *reinterpret_cast<f32x4*>(sLa + r * D + 4 * cq) = r < len ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
   // inputs: thread c < D owns key channel c (its cumulative decay and the
   // key-side factors); thread D + c copies value channel c of v and dO
   if (tid < D) {
@@ -181,17 +362,30 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
     // e^(G_r - G_s) would inherit as a relative one
     double gs = 0.0, a = 0.0;
     for (int r = 0; r < C; ++r) {
-      gs += r < len ? (double)log_alpha[((t0 + r) * H + h) * D + c] : 0.0;
+      gs += (double)sLa[r * D + c];
       if (r == 31) a = gs;   // the anchor: mid-chunk
     }
     const double gC = gs;
-    B[L::GAM + c] = (float)exp(gC);
+    const double ea = exp(a), egc = exp(gC);
+    B[L::GAM + c] = (float)egc;
     double G = 0.0;   // the same sums again, in the same order
-    for (int r = 0; r < C; ++r) {
-      const int64_t gi = ((t0 + r) * H + h) * D + c;
-      const float kk = r < len ? ld(k, gi) : 0.f, qq = r < len ? ld(q, gi) : 0.f;
-      G += r < len ? (double)log_alpha[gi] : 0.0;
-      const float eGa = (float)exp(G - a), eaG = (float)exp(a - G), eG = (float)exp(G), eC = (float)exp(gC - G);
+    for (int r0 = 0; r0 < C; r0 += 8) {
+      float k8[8], q8[8];   // eight rows' loads issued before any use
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t gi = ((t0 + min(r0 + i, len - 1)) * H + h) * D + c;
+        k8[i] = ld(k, gi);
+        q8[i] = ld(q, gi);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+      const int r = r0 + i;
+      const float kk = r < len ? k8[i] : 0.f, qq = r < len ? q8[i] : 0.f;
+      G += (double)sLa[r * D + c];
+      // one exponential per element; the other three factors follow from it
+      // in fp64 (each product adds one fp64 rounding)
+      const double xGa = exp(G - a), xaG = 1.0 / xGa;
+      const float eGa = (float)xGa, eaG = (float)xaG, eG = (float)(xGa * ea), eC = (float)(egc * xaG / ea);
       const int64_t o = (int64_t)r * D + c;
       B[L::KX + o] = kk;
       B[L::QX + o] = qq;
@@ -205,17 +399,29 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
       B[L::KG + o] = kk * eG;
       B[L::QG + o] = qq * eG;
       B[L::KC + o] = kk * eC;
+      }
     }
   } else if (tid < 2 * D) {
     const int c = tid - D;
-    for (int r = 0; r < C; ++r) {
-      const int64_t gi = ((t0 + r) * H + h) * D + c;
-      B[L::VX + (int64_t)r * D + c] = r < len ? ld(v, gi) : 0.f;
-      B[L::DOX + (int64_t)r * D + c] = r < len ? ld(grad_o, gi) : 0.f;
+    for (int r0 = 0; r0 < C; r0 += 16) {
+      float v16[16], o16[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t gi = ((t0 + min(r0 + i, len - 1)) * H + h) * D + c;
+        v16[i] = ld(v, gi);
+        o16[i] = ld(grad_o, gi);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = r0 + i;
+        B[L::VX + (int64_t)r * D + c] = r < len ? v16[i] : 0.f;
+        B[L::DOX + (int64_t)r * D + c] = r < len ? o16[i] : 0.f;
+      }
     }
   }
   if (tid < C) {
-    const float b = tid < len ? ld(beta, (t0 + tid) * H + h) : 0.f;
+    const float b1 = ld(beta, (t0 + min(tid, len - 1)) * H + h);
+    const float b = tid < len ? b1 : 0.f;
     B[L::BETA + tid] = b;
     sBeta[tid] = b;
   }
@@ -231,12 +437,22 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
              [&](int r, int s, float x) { B[L::BQ + r * C + s] = s <= r ? x : 0.f; });
 
   // T = (I + Diag(beta) A)^-1: columns are independent; lane j of wave 0
-  // walks down column j (T[r][j] = -beta_r sum_{j <= s < r} A[r][s] T[s][j])
+  // walks down column j (T[r][j] = -beta_r sum_{j <= s < r} A[r][s] T[s][j]).
+  // Entries above the diagonal are stored as zeros, so the sum may run over
+  // every s < r without a test; four partial sums keep the loads in flight.
   if (tid < C) {
     const int j = tid;
     for (int r = 0; r < C; ++r) {
-      float acc = 0.f;
-      for (int s = 0; s < r; ++s) acc += s >= j ? sA[r * C + s] * sT[s * C + j] : 0.f;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      int s = 0;
+      for (; s + 4 <= r; s += 4) {
+        a0 += sA[r * C + s] * sT[s * C + j];
+        a1 += sA[r * C + s + 1] * sT[(s + 1) * C + j];
+        a2 += sA[r * C + s + 2] * sT[(s + 2) * C + j];
+        a3 += sA[r * C + s + 3] * sT[(s + 3) * C + j];
+      }
+      for (; s < r; ++s) a0 += sA[r * C + s] * sT[s * C + j];
+      const float acc = (a0 + a1) + (a2 + a3);
       sT[r * C + j] = r == j ? 1.f : (r > j ? -sBeta[r] * acc : 0.f);
     }
   }
@@ -276,9 +492,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ cu, int N, int H,
                                                     const float* __restrict__ init, float* __restrict__ ws) {
   using L = Ws<D>;
-  constexpr int KTW = D / 64, LW = C + 16, LK = D + 16;
-  __shared__ __align__(16) float sWt[D * LW];   // W^T  [key][token]
-  __shared__ __align__(16) float sKc[C * LK];   // Kc   [token][key]
+  // LDS strides: W is read as the A operand over (token, key) pairs and Kc as
+  // the A operand over (key, token) pairs; D + 2 and D + 16 make both reads
+  // free of bank conflicts
+  constexpr int KTW = D / 64, LW = D + 2, LK = D + 16;
+  __shared__ __align__(16) float sW[C * LW];    // W  [token][key]
+  __shared__ __align__(16) float sKc[C * LK];   // Kc [token][key]
   __shared__ __align__(16) float sS[D * 16];    // S slice [key][col]
   __shared__ __align__(16) float sE[C * 16];    // E slice [token][col]
   int n, h, vt;
@@ -296,8 +515,40 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
     S[kt] = init ? *reinterpret_cast<const f32x4*>(init + (((int64_t)n * H + h) * D + col) * D + key0)
                  : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the next chunk's operands are loaded into registers while this chunk is
+  // computed: W and Kc (NQ quads each per thread), this lane's U and e^gC
+  constexpr int NQ = C * D / 4 / kThreads;
+  f32x4 pw[NQ], pk[NQ], pg[KTW];
+  float pu[4];
+  auto fetch = [&](int c) {
+    const float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+      pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
+      pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pu[i] = B[L::U + (int64_t)(16 * w + 4 * g + i) * D + col];
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
+  };
+  if (nch > 0) fetch(0);
   for (int c = 0; c < nch; ++c) {
     float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+      *reinterpret_cast<float2*>(sW + r * LW + 4 * cq) = float2{pw[i][0], pw[i][1]};
+      *reinterpret_cast<float2*>(sW + r * LW + 4 * cq + 2) = float2{pw[i][2], pw[i][3]};
+      *reinterpret_cast<f32x4*>(sKc + r * LK + 4 * cq) = pk[i];
+    }
+    float u[4];
+    f32x4 gam[KTW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = pu[i];
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) gam[kt] = pg[kt];
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt) + 4 * g;
@@ -305,22 +556,16 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(key0 + i) * 16 + l16] = S[kt][i];
     }
-    for (int idx = tid; idx < C * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), cq = idx % (D / 4);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sWt[(4 * cq + i) * LW + r] = x[i];
-      *reinterpret_cast<f32x4*>(sKc + r * LK + 4 * cq) = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
-    }
+    if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     // E = U - W S for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sWt[(k0 + g) * LW + 16 * w + l16], sS[(k0 + g) * 16 + l16], acc);
+    for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sW[(16 * w + l16) * LW + k0 + g], sS[(k0 + g) * 16 + l16], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * g + i;
-      const float e = B[L::U + (int64_t)r * D + col] - acc[i];
+      const float e = u[i] - acc[i];
       B[L::E + (int64_t)r * D + col] = e;
       sE[r * 16 + l16] = e;
     }
@@ -329,8 +574,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[kt][i] *= B[L::GAM + key0 + 4 * g + i];
+      S[kt] *= gam[kt];
 #pragma unroll 4
       for (int t = 0; t < C; t += 4) S[kt] = mfma4(sKc[(t + g) * LK + key0 + l16], sE[(t + g) * 16 + l16], S[kt]);
     }
@@ -347,17 +591,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
                                                        const float* __restrict__ grad_final,
                                                        float* __restrict__ grad_init, float* __restrict__ ws) {
   using L = Ws<D>;
-  constexpr int KTW = D / 64, LC = C + 16, LK = D + 16;
-  // phase 1: Bq [s][token] and Kc^T [key][token]; phase 2: Qg, W [token][key]
-  constexpr int REGION = (C * LC + D * LC) > (2 * C * LK) ? (C * LC + D * LC) : (2 * C * LK);
-  __shared__ __align__(16) float sX[REGION];
+  // LDS strides chosen so that every MFMA operand read is conflict-free:
+  // Bq is read over (token, s) pairs, Kc over (token, key), Qg and W over
+  // (key, token)
+  constexpr int KTW = D / 64, LC = C + 16, LK = D + 16, LR = D + 2;
+  __shared__ __align__(16) float sBq[C * LC];   // Bq [s][token]
+  __shared__ __align__(16) float sKc[C * LR];   // Kc [token][key]
+  __shared__ __align__(16) float sQg[C * LK];   // Qg [token][key]
+  __shared__ __align__(16) float sW[C * LK];    // W  [token][key]
   __shared__ __align__(16) float sdO[C * 16];
   __shared__ __align__(16) float sdS[D * 16];
   __shared__ __align__(16) float snE[C * 16];
-  float* sBq = sX;
-  float* sKcT = sX + C * LC;
-  float* sQg = sX;
-  float* sW = sX + C * LK;
   int n, h, vt;
   if (!slice_of<D>(N, H, n, h, vt)) return;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
@@ -373,8 +617,48 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
     const int key0 = 16 * (w * KTW + kt) + 4 * g;
     dS[kt] = grad_final ? *reinterpret_cast<const f32x4*>(grad_final + sbase + key0) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the previous chunk's operands are loaded into registers while this one
+  // is computed
+  constexpr int NQ = C * D / 4 / kThreads, NB = C * C / 4 / kThreads;
+  f32x4 pb[NB], pk[NQ], pq[NQ], pw[NQ], po, pg[KTW];
+  auto fetch = [&](int c) {
+    const float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
+      pb[i] = *reinterpret_cast<const f32x4*>(B + L::BQ + s * C + 4 * tq);
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+      pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
+      pq[i] = *reinterpret_cast<const f32x4*>(B + L::QG + (int64_t)r * D + 4 * cq);
+      pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
+    }
+    po = *reinterpret_cast<const f32x4*>(B + L::DOX + (int64_t)(tid >> 2) * D + 16 * vt + 4 * (tid & 3));
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
+  };
+  if (nch > 0) fetch(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
+      *reinterpret_cast<f32x4*>(sBq + s * LC + 4 * tq) = pb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+      *reinterpret_cast<float2*>(sKc + r * LR + 4 * cq) = float2{pk[i][0], pk[i][1]};
+      *reinterpret_cast<float2*>(sKc + r * LR + 4 * cq + 2) = float2{pk[i][2], pk[i][3]};
+      *reinterpret_cast<f32x4*>(sQg + r * LK + 4 * cq) = pq[i];
+      *reinterpret_cast<f32x4*>(sW + r * LK + 4 * cq) = pw[i];
+    }
+    *reinterpret_cast<f32x4*>(sdO + (tid >> 2) * 16 + 4 * (tid & 3)) = po;
+    f32x4 gam[KTW];
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) gam[kt] = pg[kt];
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt) + 4 * g;
@@ -382,28 +666,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) sdS[(key0 + i) * 16 + l16] = dS[kt][i];
     }
-    for (int idx = tid; idx < C * C / 4; idx += kThreads) {
-      const int s = idx / (C / 4), tq = idx % (C / 4);
-      *reinterpret_cast<f32x4*>(sBq + s * LC + 4 * tq) = *reinterpret_cast<const f32x4*>(B + L::BQ + s * C + 4 * tq);
-    }
-    for (int idx = tid; idx < C * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), cq = idx % (D / 4);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sKcT[(4 * cq + i) * LC + r] = x[i];
-    }
-    if (tid < C * 4) {
-      const int r = tid >> 2, qd = tid & 3;
-      *reinterpret_cast<f32x4*>(sdO + r * 16 + 4 * qd) =
-          *reinterpret_cast<const f32x4*>(B + L::DOX + (int64_t)r * D + 16 * vt + 4 * qd);
-    }
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     // dE = Bq^T dO + Kc dS for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int s = 0; s < C; s += 4) acc = mfma4(sBq[(s + g) * LC + 16 * w + l16], sdO[(s + g) * 16 + l16], acc);
 #pragma unroll 8
-    for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sKcT[(k0 + g) * LC + 16 * w + l16], sdS[(k0 + g) * 16 + l16], acc);
+    for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sKc[(16 * w + l16) * LR + k0 + g], sdS[(k0 + g) * 16 + l16], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * g + i;
@@ -411,18 +681,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
       snE[r * 16 + l16] = -acc[i];
     }
     __syncthreads();
-    for (int idx = tid; idx < C * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), cq = idx % (D / 4);
-      *reinterpret_cast<f32x4*>(sQg + r * LK + 4 * cq) = *reinterpret_cast<const f32x4*>(B + L::QG + (int64_t)r * D + 4 * cq);
-      *reinterpret_cast<f32x4*>(sW + r * LK + 4 * cq) = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
-    }
-    __syncthreads();
     // dS <- Diag(gamma) dS + Qg^T dO - W^T dE
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dS[kt][i] *= B[L::GAM + key0 + 4 * g + i];
+      dS[kt] *= gam[kt];
 #pragma unroll 4
       for (int t = 0; t < C; t += 4) {
         dS[kt] = mfma4(sQg[(t + g) * LK + key0 + l16], sdO[(t + g) * 16 + l16], dS[kt]);
@@ -444,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 // Kernel 4: per-(chunk, head) gradients.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
+__global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
                                                      float* __restrict__ ws, float* __restrict__ gq,
                                                      float* __restrict__ gk, float* __restrict__ gv,
                                                      float* __restrict__ gla, float* __restrict__ gbeta) {
@@ -459,87 +722,101 @@ __global__ __launch_bounds__(kThreads) void bwd_grad(const int32_t* __restrict__
   const float* beta = B + L::BETA;
   double* dG = reinterpret_cast<double*>(B + L::DG);
   auto at = [&](int64_t base, int r, int c) -> float& { return B[base + (int64_t)r * D + c]; };
-  // dG accumulates exact fp64 products of fp32 factors
-  auto addG = [&](int r, int c, float x, int64_t factor) {
-    dG[(int64_t)r * D + c] += (double)x * (double)at(factor, r, c);
-  };
+  auto M = [&](int64_t base, int rs, int cs) { return Mat{B + base, rs, cs}; };
+  auto F = [&](int64_t base) { return B + base; };
 
-  // dQg = dO S0^T: dQ = dQg e^G, dG = dQg o Qg
-  wg_gemm<D>(Mat{B + L::DOX, D, 1}, Mat{B + L::S0, D, 1}, D, lds, [&](int r, int c, float x) {
-    at(L::DQ, r, c) = x * at(L::EG, r, c);
-    dG[(int64_t)r * D + c] = (double)x * (double)at(L::QG, r, c);
-  });
-  // dKc = E dS_end^T: dK = dKc e^(gC-G), dG -= dKc o Kc
-  wg_gemm<D>(Mat{B + L::E, D, 1}, Mat{B + L::DS, D, 1}, D, lds, [&](int r, int c, float x) {
-    at(L::DKC, r, c) = x;
-    at(L::DK, r, c) = x * at(L::EC, r, c);
-    addG(r, c, -x, L::KC);
-  });
-  // dW = -dE S0^T
-  wg_gemm<D>(Mat{B + L::DE, D, 1}, Mat{B + L::S0, D, 1}, D, lds,
-             [&](int r, int c, float x) { at(L::DW, r, c) = -x; });
   // dBq = lower(dO E^T), kept as its strict lower part and its diagonal:
   // Bq[r][r] = q_r . k_r carries no decay, so its terms would enter dG twice
   // with opposite signs; they go straight to dq and dk instead
-  wg_gemm<C>(Mat{B + L::DOX, D, 1}, Mat{B + L::E, 1, D}, D, lds, [&](int r, int s, float x) {
+  wg_gemm<C>(M(L::DOX, D, 1), M(L::E, 1, D), D, lds, [&](int r, int s, float x) {
     B[L::DBQ + r * C + s] = s < r ? x : 0.f;
     if (s == r) B[L::DBQD + r] = x;
   });
-  // P = T^T dE: dV = Diag(beta) P
-  wg_gemm<D>(Mat{B + L::T, 1, C}, Mat{B + L::DE, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::P, r, c) = x;
-    if (r < len) gv[((t0 + r) * H + h) * D + c] = beta[r] * x;
-  });
-  // R = T^T dW: dKg = Diag(beta) R: dK += dKg e^G, dG += dKg o Kg
-  wg_gemm<D>(Mat{B + L::T, 1, C}, Mat{B + L::DW, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::R, r, c) = x;
-    const float dkg = beta[r] * x;
-    at(L::DK, r, c) += dkg * at(L::EG, r, c);
-    addG(r, c, dkg, L::KG);
-  });
-  // dT = dE (Diag(beta) V)^T + dW (Diag(beta) Kg)^T
-  wg_gemm<C>(Mat{B + L::DE, D, 1}, Mat{B + L::VX, 1, D}, D, lds,
-             [&](int r, int s, float x) { B[L::DT + r * C + s] = beta[s] * x; });
-  wg_gemm<C>(Mat{B + L::DW, D, 1}, Mat{B + L::KG, 1, D}, D, lds,
-             [&](int r, int s, float x) { B[L::DT + r * C + s] += beta[s] * x; });
+  {  // dQg = dO S0^T: dQ = dQg e^G, dG = dQg o Qg
+    EpiD e;
+    e.x = F(L::DQ); e.fx = F(L::EG);
+    e.dg = dG; e.fg = F(L::QG);
+    gemm_d<D>(M(L::DOX, D, 1), M(L::S0, D, 1), D, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // dQa = dBs Kb: dQ += dQa e^(G-a), dG += dQa o Qa
+    EpiD e;
+    e.x = F(L::DQ); e.fx = F(L::EGA); e.x_add = true;
+    e.dg = dG; e.fg = F(L::QA); e.g_add = true;
+    gemm_d<D>(M(L::DBQ, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // dKc = E dS_end^T: dK = dKc e^(gC-G), dG -= dKc o Kc
+    EpiD e;
+    e.store = F(L::DKC);
+    e.x = F(L::DK); e.fx = F(L::EC);
+    e.dg = dG; e.fg = F(L::KC); e.g_add = true; e.g_sign = -1.f;
+    gemm_d<D>(M(L::E, D, 1), M(L::DS, D, 1), D, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // dW = -dE S0^T
+    EpiD e;
+    e.store = F(L::DW); e.store_scale = -1.f;
+    gemm_d<D>(M(L::DE, D, 1), M(L::S0, D, 1), D, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // P = T^T dE: dV = Diag(beta) P
+    EpiD e;
+    e.store = F(L::P);
+    e.out = gv + (t0 * H + h) * D; e.out_rs = (int64_t)H * D; e.len = len; e.beta = beta;
+    gemm_d<D>(M(L::T, 1, C), M(L::DE, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // R = T^T dW: dKg = Diag(beta) R: dK += dKg e^G, dG += dKg o Kg
+    EpiD e;
+    e.store = F(L::R);
+    e.x = F(L::DK); e.fx = F(L::EG); e.x_add = true;
+    e.dg = dG; e.fg = F(L::KG); e.g_add = true;
+    e.row_beta = true; e.beta = beta;
+    gemm_d<D>(M(L::T, 1, C), M(L::DW, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  }
+  // dT = dE (Diag(beta) V)^T + dW (Diag(beta) Kg)^T  (beta of the column)
+  {
+    f32x4 a[C / 16];
+    wg_mm<C>(M(L::DE, D, 1), M(L::VX, 1, D), D, M(L::DW, D, 1), M(L::KG, 1, D), D, lds, a);
+    const int w = threadIdx.x >> 6, g = (threadIdx.x & 63) >> 4, l16 = threadIdx.x & 15;
+#pragma unroll
+    for (int nt = 0; nt < C / 16; ++nt) {
+      const float bc = beta[16 * nt + l16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) B[L::DT + (16 * w + 4 * g + i) * C + 16 * nt + l16] = bc * a[nt][i];
+    }
+  }
   // X = dT T^T; dM = -T^T X: dA = strict_lower(Diag(beta) dM), dMA = strict_lower(dM) o A
-  wg_gemm<C>(Mat{B + L::DT, C, 1}, Mat{B + L::T, 1, C}, C, lds,
-             [&](int r, int s, float x) { B[L::X + r * C + s] = x; });
-  wg_gemm<C>(Mat{B + L::T, 1, C}, Mat{B + L::X, C, 1}, C, lds, [&](int r, int s, float x) {
+  wg_gemm<C>(M(L::DT, C, 1), M(L::T, 1, C), C, lds, [&](int r, int s, float x) { B[L::X + r * C + s] = x; });
+  wg_gemm<C>(M(L::T, 1, C), M(L::X, C, 1), C, lds, [&](int r, int s, float x) {
     const float dm = -x;
     B[L::DA + r * C + s] = s < r ? beta[r] * dm : 0.f;
     B[L::DMA + r * C + s] = s < r ? dm * B[L::A + r * C + s] : 0.f;
   });
-  // dKa = dA Kb: dK += dKa e^(G-a), dG += dKa o Ka
-  wg_gemm<D>(Mat{B + L::DA, C, 1}, Mat{B + L::KB, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::DK, r, c) += x * at(L::EGA, r, c);
-    addG(r, c, x, L::KA);
-  });
-  // dKb = dA^T Ka + dBq^T Qa (strict parts): dK += dKb e^(a-G), dG -= dKb o Kb
-  wg_gemm<D>(Mat{B + L::DA, 1, C}, Mat{B + L::KA, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::DK, r, c) += x * at(L::EAG, r, c);
-    addG(r, c, -x, L::KB);
-  });
-  wg_gemm<D>(Mat{B + L::DBQ, 1, C}, Mat{B + L::QA, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::DK, r, c) += x * at(L::EAG, r, c);
-    addG(r, c, -x, L::KB);
-  });
-  // dQa = dBq Kb (strict part): dQ += dQa e^(G-a), dG += dQa o Qa
-  wg_gemm<D>(Mat{B + L::DBQ, C, 1}, Mat{B + L::KB, D, 1}, C, lds, [&](int r, int c, float x) {
-    at(L::DQ, r, c) += x * at(L::EGA, r, c);
-    addG(r, c, x, L::QA);
-  });
+  {  // dKa = dA Kb: dK += dKa e^(G-a), dG += dKa o Ka
+    EpiD e;
+    e.x = F(L::DK); e.fx = F(L::EGA); e.x_add = true;
+    e.dg = dG; e.fg = F(L::KA); e.g_add = true;
+    gemm_d<D>(M(L::DA, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  }
+  {  // dKb = dA^T Ka + dBs^T Qa: dK += dKb e^(a-G), dG -= dKb o Kb
+    EpiD e;
+    e.x = F(L::DK); e.fx = F(L::EAG); e.x_add = true;
+    e.dg = dG; e.fg = F(L::KB); e.g_add = true; e.g_sign = -1.f;
+    gemm_d<D>(M(L::DA, 1, C), M(L::KA, D, 1), C, M(L::DBQ, 1, C), M(L::QA, D, 1), C, lds, e);
+  }
+  __syncthreads();
 
-  // element-wise assembly: thread c < D owns key channel c
-  const int tid = threadIdx.x;
+  // element-wise assembly: thread c < D owns key channel c (loops unrolled
+  // so that each thread keeps many independent loads in flight)
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   if (tid < D) {
     const int c = tid;
     double dgam = 0.0;
+#pragma unroll 16
     for (int j = 0; j < D; ++j)
       dgam += (double)B[L::DS + (int64_t)j * D + c] * (double)B[L::S0 + (int64_t)j * D + c];
     double dgc = dgam * (double)B[L::GAM + c];
+#pragma unroll 16
     for (int r = 0; r < C; ++r) dgc += (double)at(L::DKC, r, c) * (double)at(L::KC, r, c);
     double suf = 0.0;
+#pragma unroll 8
     for (int r = C - 1; r >= 0; --r) {
       suf += dG[(int64_t)r * D + c];
       if (r < len) {
@@ -550,14 +827,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grad(const int32_t* __restrict__
         gk[o] = at(L::DK, r, c) + dd * at(L::QX, r, c);
       }
     }
-  } else if (tid < D + C) {
-    const int r = tid - D;
-    if (r < len) {
-      float db = 0.f;
-      for (int j = 0; j < D; ++j) db += at(L::P, r, j) * at(L::VX, r, j) + at(L::R, r, j) * at(L::KG, r, j);
-      for (int s = 0; s < r; ++s) db += B[L::DMA + r * C + s];
-      gbeta[(t0 + r) * H + h] = db;
-    }
+  }
+  // dbeta: wave w reduces rows [16 w, 16 w + 16), its lanes across columns
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int r = 16 * w + rr;
+    float part = 0.f;
+#pragma unroll
+    for (int j = l; j < D; j += 64) part += at(L::P, r, j) * at(L::VX, r, j) + at(L::R, r, j) * at(L::KG, r, j);
+    part += B[L::DMA + r * C + l];   // strictly lower: zero for l >= r
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (l == 0 && r < len) gbeta[(t0 + r) * H + h] = part;
   }
 }
 
