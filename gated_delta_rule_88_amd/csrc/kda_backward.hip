@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 // Kernel 4: per-(chunk, head) gradients.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
+__global__ __launch_bounds__(kThreads, 3) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
                                                      float* __restrict__ ws, float* __restrict__ gq,
                                                      float* __restrict__ gk, float* __restrict__ gv,
                                                      float* __restrict__ gla, float* __restrict__ gbeta) {
@@ -803,28 +803,57 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
   }
   __syncthreads();
 
-  // element-wise assembly: thread c < D owns key channel c (loops unrolled
-  // so that each thread keeps many independent loads in flight)
+  // element-wise assembly.  Thread t owns key channel c = t % D and one of
+  // NG = 256 / D groups of rows; group partial sums meet in LDS (fixed order).
+  constexpr int NG = kThreads / D, RG = C / NG, JG = D / NG;
+  double* sRed = reinterpret_cast<double*>(lds);   // [NG][D]: partials, then group totals
+  double* sDgc = sRed + NG * D;                     // [D]
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  if (tid < D) {
-    const int c = tid;
-    double dgam = 0.0;
+  const int c = tid % D, grp = tid / D;
+  {
+    double dgam = 0.0, dkc = 0.0;
 #pragma unroll 16
-    for (int j = 0; j < D; ++j)
+    for (int j = grp * JG; j < (grp + 1) * JG; ++j)
       dgam += (double)B[L::DS + (int64_t)j * D + c] * (double)B[L::S0 + (int64_t)j * D + c];
-    double dgc = dgam * (double)B[L::GAM + c];
 #pragma unroll 16
-    for (int r = 0; r < C; ++r) dgc += (double)at(L::DKC, r, c) * (double)at(L::KC, r, c);
-    double suf = 0.0;
-#pragma unroll 8
-    for (int r = C - 1; r >= 0; --r) {
-      suf += dG[(int64_t)r * D + c];
+    for (int r = grp * RG; r < (grp + 1) * RG; ++r) dkc += (double)at(L::DKC, r, c) * (double)at(L::KC, r, c);
+    // partial of dgC = rowsum(dS_end o S0) gamma + colsum(dKc o Kc)
+    sRed[grp * D + c] = dgam * (double)B[L::GAM + c] + dkc;
+  }
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+    for (int x = 0; x < NG; ++x) t += sRed[x * D + tid];
+    sDgc[tid] = t;
+  }
+  // d log_alpha[r] = sum_{s >= r} dG[s] + dgC: each group sums its own rows
+  // bottom-up, then adds the totals of the groups below it
+  double suf[RG];
+  {
+    double acc2 = 0.0;
+#pragma unroll
+    for (int x = RG - 1; x >= 0; --x) {
+      acc2 += dG[(int64_t)(grp * RG + x) * D + c];
+      suf[x] = acc2;
+    }
+    __syncthreads();   // sRed partials consumed
+    sRed[grp * D + c] = acc2;
+  }
+  __syncthreads();
+  {
+    double later = sDgc[c];
+    for (int x = grp + 1; x < NG; ++x) later += sRed[x * D + c];
+#pragma unroll
+    for (int x = 0; x < RG; ++x) {
+      const int r = grp * RG + x;
+      const float dd = B[L::DBQD + r];
+      const float gqv = at(L::DQ, r, c) + dd * at(L::KX, r, c);
+      const float gkv = at(L::DK, r, c) + dd * at(L::QX, r, c);
       if (r < len) {
         const int64_t o = ((t0 + r) * H + h) * D + c;
-        const float dd = B[L::DBQD + r];
-        gla[o] = (float)(suf + dgc);
-        gq[o] = at(L::DQ, r, c) + dd * at(L::KX, r, c);
-        gk[o] = at(L::DK, r, c) + dd * at(L::QX, r, c);
+        gla[o] = (float)(suf[x] + later);
+        gq[o] = gqv;
+        gk[o] = gkv;
       }
     }
   }
