@@ -109,11 +109,14 @@ __device__ __forceinline__ float row_shr(float v) {   // lane i of a DPP row get
 // product over keys and, lane for lane, the accumulator tiles of the
 // transposed (key x token) matrix for key tiles 2p and 2p + 1.
 // ---------------------------------------------------------------------------
-template <int D>
+// SCALAR: one gate per (token, head) instead of one per key channel; RAW: q,
+// k unnormalised and beta a logit (normalised in the kernel).  Both are
+// compile-time so that the input loads carry no branch.
+template <int D, bool SCALAR, bool RAW>
 __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
-    int N, int H, unsigned char* __restrict__ ws, int scalar_gate, int raw_qkb) {
+    int N, int H, unsigned char* __restrict__ ws) {
   using R = Rec<D>;
   using L = PrepLds<D>;
   constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
@@ -142,33 +145,41 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   // ---- inputs in row layout --------------------------------------------------
   bf16x4 kr[KB][2], qr[KB][2], vr[KB][2];
   f32x4 gr[KB][2];
-  float bt = 0.f;
+  float bt;
   {
+    // every lane loads from a token clamped into the chunk and zeroes what
+    // lies past its end afterwards: no load is conditional, so all of them
+    // are in flight together
     const bool valid = r < len;
-    const int64_t base = ((t0 + r) * H + h) * D;
+    const int64_t row = t0 + min(r, len - 1);
+    const int64_t base = (row * H + h) * D;
+    const bf16x4 z4 = bf16x4{(In)0.f, (In)0.f, (In)0.f, (In)0.f};
     // one gate per (token, head): the same log decay for every key channel
-    const float g1 = (valid && scalar_gate) ? log_alpha[(t0 + r) * H + h] : 0.f;
+    float g1 = 0.f;
+    if constexpr (SCALAR) g1 = log_alpha[row * H + h];
 #pragma unroll
     for (int p = 0; p < KB; ++p)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int key = 32 * p + 16 * hh + 4 * g;
-        kr[p][hh] = qr[p][hh] = vr[p][hh] = bf16x4{(In)0.f, (In)0.f, (In)0.f, (In)0.f};
-        gr[p][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (valid) {
-          kr[p][hh] = *reinterpret_cast<const bf16x4*>(k + base + key);
-          qr[p][hh] = *reinterpret_cast<const bf16x4*>(q + base + key);
-          vr[p][hh] = *reinterpret_cast<const bf16x4*>(v + base + key);
-          gr[p][hh] = scalar_gate ? f32x4{g1, g1, g1, g1}
-                                  : *reinterpret_cast<const f32x4*>(log_alpha + base + key);
-        }
+        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(k + base + key);
+        const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(q + base + key);
+        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(v + base + key);
+        f32x4 g4;
+        if constexpr (SCALAR) g4 = f32x4{g1, g1, g1, g1};
+        else g4 = *reinterpret_cast<const f32x4*>(log_alpha + base + key);
+        kr[p][hh] = valid ? k1 : z4;
+        qr[p][hh] = valid ? q1 : z4;
+        vr[p][hh] = valid ? v1 : z4;
+        gr[p][hh] = valid ? g4 : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    if (valid) bt = (float)beta[(t0 + r) * H + h];
+    const float b1 = (float)beta[row * H + h];
+    bt = valid ? b1 : 0.f;
   }
   // raw inputs: unit q and k per token (the token's keys sit in lanes
   // l16 + 16 g, g = 0..3) and beta from its logit
   float rk = 1.f, rq = 1.f;
-  if (raw_qkb) {
+  if constexpr (RAW) {
     float ksq = 0.f, qsq = 0.f;
 #pragma unroll
     for (int p = 0; p < KB; ++p)
@@ -698,10 +709,11 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   const int64_t items = slots * A.num_heads;
   if (A.total_tokens > 0) {
-    hipLaunchKernelGGL((prep_kernel<D>), dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
+    auto kern = A.scalar_gate ? (A.raw_qkb ? prep_kernel<D, true, true> : prep_kernel<D, true, false>)
+                              : (A.raw_qkb ? prep_kernel<D, false, true> : prep_kernel<D, false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                        (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens,
-                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace, (int)A.scalar_gate,
-                       (int)A.raw_qkb);
+                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
