@@ -12,6 +12,10 @@ Prints one JSON line:
   ms_per_step  wall time of one whole step (prefill + decode step)
   decode       decode state GB/s and tokens/s from HIP events around each step
   roofline     the call with the larger share of the step, against its bound
+  varlen_16, long_1m
+               the variable-length (16 sequences, lengths U[512, 32768], random
+               initial states) and long-context (one 2^20-token sequence,
+               H = 16) prefill workloads: tokens/s and HBM fraction per call
   backward     kda_prefill_backward on the 8K workload (gradients of every
                input for seeded upstream gradients), against the fp32 MFMA peak
   cpu_baseline the fp64 oracle on the host cores, same prefill workload
@@ -364,6 +368,42 @@ def main():
         torch.cuda.synchronize()
         seq_ms.append(e0.elapsed_time(e1) / seq_steps)
 
+    # the other two prefill workloads, each timed on its own after one
+    # untimed call; inputs are drawn on the GPU and freed afterwards
+    def workload_leg(name, calls):
+        wl = inputs.WORKLOADS[name]
+        X = inputs.prefill_inputs(wl, device=dev)
+        Tw, Hw, Dw = X["q"].shape
+        Nw = X["cu_seqlens"].shape[0] - 1
+        ow = torch.empty((Tw, Hw, Dw), device=dev, dtype=torch.bfloat16)
+        fw = torch.empty((Nw, Hw, Dw, Dw), device=dev, dtype=torch.float32)
+        ww = torch.empty(kda.workspace_size(Nw, Tw, Hw, Dw, Dw, torch.bfloat16), device=dev, dtype=torch.uint8)
+
+        def run():
+            kda.kda_prefill_varlen(X["q"], X["k"], X["v"], X["log_alpha"], X["beta"], X["cu_seqlens"],
+                                   X["init_state"], o=ow, final_state=fw, workspace=ww)
+
+        run()
+        evw = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(calls)]
+        for e in evw:
+            e[0].record()
+            run()
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in evw]
+        avg = sum(ms) / len(ms)
+        wbytes, _ = prefill_algorithmic(Tw, Hw, Dw, Nw, X["init_state"] is not None, True)
+        rec = {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "calls": calls, "tokens": Tw, "sequences": Nw,
+               "heads": Hw, "tokens_per_s": round(Tw / (avg * 1e-3), 1),
+               "GB_s": round(wbytes / (avg * 1e-3) / 1e9, 1),
+               "frac_hbm": round(wbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": wbytes}
+        del X, ow, fw, ww
+        torch.cuda.empty_cache()
+        return rec
+
+    varlen_rec = workload_leg("varlen_16", 5)
+    long_rec = workload_leg("long_1m", 3)
+
     # backward, timed on its own (fewer repeats: it is the longest call)
     Kb = max(3, K // 4)
     for _ in range(min(args.warmup, 2)):
@@ -441,6 +481,8 @@ def main():
                           "value": round(dbytes / (sum(pool_ms) / K * 1e-3) / 1e9, 1), "unit": "GB/s",
                           "pool_slots": 2 * dwl.num_seqs,
                           "launch": "kda_decode_step_pooled: decode_step_kernel with a slot map"},
+        "varlen_16": varlen_rec,
+        "long_1m": long_rec,
         "backward": backward_report(bwd_ms, T, H, D),
         "roofline": dominant,
     }
