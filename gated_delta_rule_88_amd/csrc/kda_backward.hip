@@ -322,7 +322,7 @@ __device__ __forceinline__ float ld(const In* p, int64_t i) { return to_f32(p[i]
 // Kernel 1: factors of one (chunk, head).
 // ---------------------------------------------------------------------------
 template <int D, class In>
-__global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, const In* __restrict__ k,
+__global__ __launch_bounds__(kThreads, 2) void bwd_prep(const In* __restrict__ q, const In* __restrict__ k,
                                                      const In* __restrict__ v, const float* __restrict__ log_alpha,
                                                      const In* __restrict__ beta, const In* __restrict__ grad_o,
                                                      const int32_t* __restrict__ cu, int N, int H,
@@ -353,69 +353,62 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
     *reinterpret_cast<f32x4*>(sLa + r * D + 4 * cq) = r < len ? x : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
-  // inputs: thread c < D owns key channel c (its cumulative decay and the
-  // key-side factors); thread D + c copies value channel c of v and dO
-  if (tid < D) {
-    const int c = tid;
+  // inputs: thread t owns key and value channel c = t % D for one of the
+  // NG = 256 / D groups of rows (its cumulative decay, the key-side factors,
+  // and the copies of v and dO)
+  {
+    constexpr int NG = kThreads / D, RG = C / NG;
+    const int c = tid % D, grp = tid / D, r0 = grp * RG;
     // the cumulative decay and its exponentials in fp64: an fp32 running sum
     // over strong decays carries an absolute error that every factor
-    // e^(G_r - G_s) would inherit as a relative one
-    double gs = 0.0, a = 0.0;
+    // e^(G_r - G_s) would inherit as a relative one.  Every thread sums from
+    // row 0 in the same order, so all groups see the same G.
+    double gs = 0.0, a = 0.0, G = 0.0;
+#pragma unroll 4
     for (int r = 0; r < C; ++r) {
       gs += (double)sLa[r * D + c];
       if (r == 31) a = gs;   // the anchor: mid-chunk
+      if (r == r0 - 1) G = gs;
     }
     const double gC = gs;
     const double ea = exp(a), egc = exp(gC);
-    B[L::GAM + c] = (float)egc;
-    double G = 0.0;   // the same sums again, in the same order
-    for (int r0 = 0; r0 < C; r0 += 8) {
-      float k8[8], q8[8];   // eight rows' loads issued before any use
+    if (grp == 0) B[L::GAM + c] = (float)egc;
+#pragma unroll 1
+    for (int x0 = 0; x0 < RG; x0 += 4) {
+      float k8[4], q8[4], v8[4], o8[4];   // four rows' loads issued before any use
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t gi = ((t0 + min(r0 + i, len - 1)) * H + h) * D + c;
+      for (int i = 0; i < 4; ++i) {
+        const int64_t gi = ((t0 + min(r0 + x0 + i, len - 1)) * H + h) * D + c;
         k8[i] = ld(k, gi);
         q8[i] = ld(q, gi);
+        v8[i] = ld(v, gi);
+        o8[i] = ld(grad_o, gi);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-      const int r = r0 + i;
-      const float kk = r < len ? k8[i] : 0.f, qq = r < len ? q8[i] : 0.f;
-      G += (double)sLa[r * D + c];
-      // one exponential per element; the other three factors follow from it
-      // in fp64 (each product adds one fp64 rounding)
-      const double xGa = exp(G - a), xaG = 1.0 / xGa;
-      const float eGa = (float)xGa, eaG = (float)xaG, eG = (float)(xGa * ea), eC = (float)(egc * xaG / ea);
-      const int64_t o = (int64_t)r * D + c;
-      B[L::KX + o] = kk;
-      B[L::QX + o] = qq;
-      B[L::EG + o] = eG;
-      B[L::EC + o] = eC;
-      B[L::EGA + o] = eGa;
-      B[L::EAG + o] = eaG;
-      B[L::KA + o] = kk * eGa;
-      B[L::KB + o] = kk * eaG;
-      B[L::QA + o] = qq * eGa;
-      B[L::KG + o] = kk * eG;
-      B[L::QG + o] = qq * eG;
-      B[L::KC + o] = kk * eC;
-      }
-    }
-  } else if (tid < 2 * D) {
-    const int c = tid - D;
-    for (int r0 = 0; r0 < C; r0 += 16) {
-      float v16[16], o16[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t gi = ((t0 + min(r0 + i, len - 1)) * H + h) * D + c;
-        v16[i] = ld(v, gi);
-        o16[i] = ld(grad_o, gi);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = r0 + i;
-        B[L::VX + (int64_t)r * D + c] = r < len ? v16[i] : 0.f;
-        B[L::DOX + (int64_t)r * D + c] = r < len ? o16[i] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + x0 + i;
+        const bool in = r < len;
+        const float kk = in ? k8[i] : 0.f, qq = in ? q8[i] : 0.f;
+        G += (double)sLa[r * D + c];
+        // one exponential per element; the other three factors follow from
+        // it in fp64 (each product adds one fp64 rounding)
+        const double xGa = exp(G - a), xaG = 1.0 / xGa;
+        const float eGa = (float)xGa, eaG = (float)xaG, eG = (float)(xGa * ea), eC = (float)(egc * xaG / ea);
+        const int64_t o = (int64_t)r * D + c;
+        B[L::KX + o] = kk;
+        B[L::QX + o] = qq;
+        B[L::VX + o] = in ? v8[i] : 0.f;
+        B[L::DOX + o] = in ? o8[i] : 0.f;
+        B[L::EG + o] = eG;
+        B[L::EC + o] = eC;
+        B[L::EGA + o] = eGa;
+        B[L::EAG + o] = eaG;
+        B[L::KA + o] = kk * eGa;
+        B[L::KB + o] = kk * eaG;
+        B[L::QA + o] = qq * eGa;
+        B[L::KG + o] = kk * eG;
+        B[L::QG + o] = qq * eG;
+        B[L::KC + o] = kk * eC;
       }
     }
   }
@@ -436,24 +429,59 @@ __global__ __launch_bounds__(kThreads) void bwd_prep(const In* __restrict__ q, c
   wg_gemm<C>(Mat{B + L::QA, D, 1}, Mat{B + L::KB, 1, D}, D, lds,
              [&](int r, int s, float x) { B[L::BQ + r * C + s] = s <= r ? x : 0.f; });
 
-  // T = (I + Diag(beta) A)^-1: columns are independent; lane j of wave 0
-  // walks down column j (T[r][j] = -beta_r sum_{j <= s < r} A[r][s] T[s][j]).
-  // Entries above the diagonal are stored as zeros, so the sum may run over
-  // every s < r without a test; four partial sums keep the loads in flight.
-  if (tid < C) {
-    const int j = tid;
-    for (int r = 0; r < C; ++r) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      int s = 0;
-      for (; s + 4 <= r; s += 4) {
-        a0 += sA[r * C + s] * sT[s * C + j];
-        a1 += sA[r * C + s + 1] * sT[(s + 1) * C + j];
-        a2 += sA[r * C + s + 2] * sT[(s + 2) * C + j];
-        a3 += sA[r * C + s + 3] * sT[(s + 3) * C + j];
+  // T = (I + Diag(beta) A)^-1 = M^-1 (unit lower triangular), by 16 x 16
+  // blocks: wave w inverts diagonal block w by substitution down its columns
+  // (lane j walks column j; entries above the diagonal are stored as zeros,
+  // so every sum runs without a test), then the blocks below the diagonal
+  // follow level by level, T_ij = -T_ii sum_{j <= k < i} M_ik T_kj with
+  // M_ik = Diag(beta) A_ik, each block by one wave.
+  {
+    const int w = tid >> 6, l = tid & 63;
+    if (l < 16) {
+      const int j = l, o = 16 * w;
+      for (int r = 0; r < 16; ++r) {
+        float a0 = 0.f, a1 = 0.f;
+        for (int s = 0; s + 1 < r; s += 2) {
+          a0 += sA[(o + r) * C + o + s] * sT[(o + s) * C + o + j];
+          a1 += sA[(o + r) * C + o + s + 1] * sT[(o + s + 1) * C + o + j];
+        }
+        if (r & 1) a0 += sA[(o + r) * C + o + r - 1] * sT[(o + r - 1) * C + o + j];
+        sT[(o + r) * C + o + j] = r == j ? 1.f : (r > j ? -sBeta[o + r] * (a0 + a1) : 0.f);
       }
-      for (; s < r; ++s) a0 += sA[r * C + s] * sT[s * C + j];
-      const float acc = (a0 + a1) + (a2 + a3);
-      sT[r * C + j] = r == j ? 1.f : (r > j ? -sBeta[r] * acc : 0.f);
+    }
+    // zeros above the diagonal blocks
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+      const int r = idx / C, c = idx % C;
+      if ((c >> 4) > (r >> 4)) sT[idx] = 0.f;
+    }
+    __syncthreads();
+    float* sX = sLa;   // [4][16][16] scratch, one tile per wave (sLa is no longer needed)
+    const int rr = l >> 2, c0 = (l & 3) * 4;
+    for (int lev = 1; lev < 4; ++lev) {
+      if (w < 4 - lev) {
+        const int bj = w, bi = w + lev;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        const float br = sBeta[16 * bi + rr];
+        for (int bk = bj; bk < bi; ++bk)
+          for (int s = 0; s < 16; ++s) {
+            const float m = br * sA[(16 * bi + rr) * C + 16 * bk + s];
+            const f32x4 t = *reinterpret_cast<const f32x4*>(sT + (16 * bk + s) * C + 16 * bj + c0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] += m * t[q];
+          }
+        *reinterpret_cast<f32x4*>(sX + w * 256 + rr * 16 + c0) = f32x4{x[0], x[1], x[2], x[3]};
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the tile is in LDS
+        __builtin_amdgcn_wave_barrier();
+        float t4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 16; ++s) {
+          const float tii = sT[(16 * bi + rr) * C + 16 * bi + s];
+          const f32x4 xs = *reinterpret_cast<const f32x4*>(sX + w * 256 + s * 16 + c0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t4[q] += tii * xs[q];
+        }
+        *reinterpret_cast<f32x4*>(sT + (16 * bi + rr) * C + 16 * bj + c0) = f32x4{-t4[0], -t4[1], -t4[2], -t4[3]};
+      }
+      __syncthreads();
     }
   }
   __syncthreads();
