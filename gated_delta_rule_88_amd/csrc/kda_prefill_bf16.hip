@@ -122,8 +122,12 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
   __shared__ __align__(16) unsigned char lds[L::BYTES];
 
+  // Slots in reverse order: the state pass starts from each sequence's first
+  // chunk, so those records, written last, are the ones most likely still
+  // held by the memory-side cache (records are stored with plain stores so
+  // that they are kept there).
   const int64_t item = blockIdx.x;
-  const int64_t slot = item / H;
+  const int64_t slot = (int64_t)(gridDim.x / H) - 1 - item / H;
   const int h = (int)(item % H);
   int n, len;
   int64_t t0;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const float tc = tm + sTot[2 * D + key] + sTot[3 * D + key];
     if (tid < D) {
       sExpK[key] = __expf(tm);
-      __builtin_nontemporal_store(__expf(tc), reinterpret_cast<float*>(rec + R::G) + key);
+      *(reinterpret_cast<float*>(rec + R::G) + key) = __expf(tc);
     } else if (tid < 2 * D) {
       sExpK[D + key] = __expf(tc - tm);
     }
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   // ---- C: A = Ka Kbar^T (tiles (w, j)) and Bqk^T = Kbar Qa^T (tiles (j, w)),
   //      j <= w, in stages of SB key blocks; Kc^T fragments to the record ----
   for (int i = tid; i < NT * 2 * 64; i += kPrepThreads)
-    __builtin_nontemporal_store(reinterpret_cast<const HFrag*>(lds + L::KCT)[i], reinterpret_cast<HFrag*>(rec + R::KC) + i);
+    *(reinterpret_cast<HFrag*>(rec + R::KC) + i) = reinterpret_cast<const HFrag*>(lds + L::KCT)[i];
   f32x4 accA[4], accB[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) accA[j] = accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
       wneg[it][e] = (In)(-wc[e]);
     }
     if (it & 1)
-      __builtin_nontemporal_store(wrec, reinterpret_cast<HFrag*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16));
+      *(reinterpret_cast<HFrag*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16)) = wrec;
   }
   __syncthreads();   // Kg^T and T are no longer read
 
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf u16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) u16[e] = (_Float16)uc[e];
-    __builtin_nontemporal_store(u16, reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8));
+    *(reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8)) = u16;
     Half uh, ul;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) qrec[4 * (it & 1) + e] = (_Float16)acc[e];
     if (it & 1)
-      __builtin_nontemporal_store(qrec, reinterpret_cast<HFrag*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16));
+      *(reinterpret_cast<HFrag*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16)) = qrec;
   }
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf bu16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bu16[e] = (_Float16)bu[e];
-    __builtin_nontemporal_store(bu16, reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8));
+    *(reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8)) = bu16;
   }
 }
 
