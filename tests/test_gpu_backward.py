@@ -62,6 +62,17 @@ def test_backward_ragged(dtype, D):
     check(d, go, gf, TOL[dtype], f"backward ragged {dtype} D={D}")
 
 
+def test_backward_many_short_sequences():
+    """257 sequences of seeded lengths 0..150 over H = 5 heads (more
+    (sequence, head) pairs than CUs, not a multiple of the block interleave)"""
+    import numpy as np
+    lengths = np.random.default_rng(480).integers(0, 151, size=257).tolist()
+    lengths[0], lengths[-1] = 0, 64
+    d = make_case(lengths, H=5, D=128, dtype=torch.bfloat16, seed=481)
+    go, gf = upstream(d, seed=482)
+    check(d, go, gf, TOL[torch.bfloat16], "backward 257 short sequences")
+
+
 def test_backward_zero_states_and_no_final_gradient():
     """init_state NULL and grad_final_state NULL; the initial-state gradient
     is still produced"""
