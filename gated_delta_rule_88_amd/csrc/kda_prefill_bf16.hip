@@ -649,7 +649,8 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
     }
     __syncthreads();
     load_ops_part<D>(nxt, nrec, 1, w, l, g, vt);
-    // token tile w: W S first -- E gates the other waves -- then Q' S
+    // token tile w: W S first -- E gates the other waves; Q' S only after
+    // the state update has been issued
     HFrag sf[KB];
 #pragma unroll
     for (int p = 0; p < KB; ++p) sf[p] = sS[p][l];
@@ -661,16 +662,6 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
 #pragma unroll
     for (int e = 0; e < 4; ++e) eh[e] = (_Float16)((float)ops.u[e] - wsum[e]);
     *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[w >> 1][l]) + 4 * (w & 1)) = eh;
-    // O = Q' S + Bqk U for token tile w
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
-#pragma unroll
-    for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[p]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * g + e;
-      if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
-    }
     __syncthreads();
     load_ops_part<D>(nxt, nrec, 2, w, l, g, vt);
     // S <- Diag(e^G[C-1]) S + Kc^T E
@@ -679,6 +670,16 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
       S[kt] *= ops.gam[kt];
 #pragma unroll
       for (int p = 0; p < 2; ++p) mma(S[kt], ops.kc[kt][p], sE[p][l]);
+    }
+    // O = Q' S + Bqk U for token tile w: off the state's dependency chain
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
+#pragma unroll
+    for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[p]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * g + e;
+      if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
     }
   };
 
