@@ -593,8 +593,11 @@ __device__ __forceinline__ void load_ops(Ops<D>& o, const unsigned char* __restr
   for (int part = 0; part < 3; ++part) load_ops_part<D>(o, rec, part, w, l, g, vt);
 }
 
+// One workgroup per CU: the pass is bound by the operand bytes a CU keeps in
+// flight, and a second workgroup on the same CU lowers the throughput of
+// both (variable-length batches with more workgroups than CUs).
 template <int D>
-__global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restrict__ cu, int N, int H,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(const int32_t* __restrict__ cu, int N, int H,
                                                          const float* init, float* fin, In* __restrict__ o,
                                                          const unsigned char* __restrict__ ws,
                                                          const int32_t* __restrict__ sidx, int pool_slots) {
@@ -686,18 +689,25 @@ __global__ __launch_bounds__(kThreads) void state_kernel(const int32_t* __restri
   // three operand buffers in rotation: while chunk c is computed, chunk
   // c+1's operands are in flight and chunk c+2's are being loaded (past the
   // last chunk the last record is read again, so every step issues the same
-  // loads and the compiler's waits stay exact)
+  // loads and the compiler's waits stay exact).  Twelve steps per loop
+  // iteration: at the loop head the compiler waits for most loads in flight,
+  // so the head is reached once every twelve chunks rather than every three.
   Ops<D> bufA, bufB, bufC;
   if (nch > 0) {
     load_ops<D>(bufA, rec_of(0), w, l, g, vt);
     load_ops<D>(bufB, rec_of(1), w, l, g, vt);
   }
-  for (int c = 0; c < nch; c += 3) {
-    step(bufA, c, bufC, rec_of(c + 2));
-    if (c + 1 >= nch) break;
-    step(bufB, c + 1, bufA, rec_of(c + 3));
-    if (c + 2 >= nch) break;
-    step(bufC, c + 2, bufB, rec_of(c + 4));
+  for (int c0 = 0; c0 < nch; c0 += 12) {
+#pragma unroll
+    for (int u = 0; u < 12; u += 3) {
+      const int c = c0 + u;
+      if (c >= nch) break;
+      step(bufA, c, bufC, rec_of(c + 2));
+      if (c + 1 >= nch) break;
+      step(bufB, c + 1, bufA, rec_of(c + 3));
+      if (c + 2 >= nch) break;
+      step(bufC, c + 2, bufB, rec_of(c + 4));
+    }
   }
 
   if (fin) {
