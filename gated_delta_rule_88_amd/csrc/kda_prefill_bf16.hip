@@ -325,8 +325,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 #pragma unroll
       for (int pb = 0; pb < SB; ++pb) {
         const int p = s * SB + pb;
-        const Frag bh = (j == w) ? kbH[p] : sKb(0, j, pb)[l];
-        const Frag bl = (j == w) ? kbL[p] : sKb(1, j, pb)[l];
+        const Frag bh = sKb(0, j, pb)[l];   // this wave's own fragments too: no
+        const Frag bl = sKb(1, j, pb)[l];   // register/LDS select per tile
         mma(accA[j], kaF[p], bh);
         mma(accB[j], bh, qaH[p]);
         mma(accB[j], bh, qaL[p]);
