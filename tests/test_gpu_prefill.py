@@ -80,6 +80,16 @@ def test_many_short_sequences(dtype, D):
     check(d, TOL[dtype], f"257 short sequences {dtype} D={D}")
 
 
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
+def test_chunk_counts_around_the_loop_unroll(dtype, D):
+    """sequences of 11, 12, 13, 24 and 25 chunks (full and partial last
+    chunks): every exit point of a chunk loop that runs several chunk steps
+    per iteration, with random initial states"""
+    lengths = [11 * 64, 12 * 64, 12 * 64 + 1, 13 * 64 - 5, 24 * 64, 25 * 64 + 3]
+    d = make_case(lengths, H=2, D=D, dtype=dtype, seed=480 + D)
+    check(d, TOL[dtype], f"chunk counts around the unroll {dtype} D={D}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_zero_initial_state_and_no_final(dtype):
     d = make_case([300], H=2, D=128, dtype=dtype, seed=7, init_std=0.0)
