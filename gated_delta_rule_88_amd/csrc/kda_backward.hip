@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 // Kernel 4: per-(chunk, head) gradients.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 3) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
+__global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
                                                      float* __restrict__ ws, float* __restrict__ gq,
                                                      float* __restrict__ gk, float* __restrict__ gv,
                                                      float* __restrict__ gla, float* __restrict__ gbeta) {
