@@ -541,33 +541,38 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 
 // ---------------------------------------------------------------------------
 // Kernel 2: sequential pass over the chunks of one (sequence, head) for a
-// 16-column slice of S.  Wave w owns key rows [D/4 w, D/4 (w+1)) of the
-// slice as accumulators and token tile w of every chunk; the operands of
-// the next two chunks are in flight while the current one is computed.
+// slice of VT value tiles (16 VT columns) of S.  Wave w owns key rows
+// [D/4 w, D/4 (w+1)) of the slice as accumulators and token tile w of every
+// chunk; the operands of the next two chunks are in flight while the
+// current one is computed.  W, Q' and Kc serve every value tile of the
+// slice, so a wider slice loads them once for more columns.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int VT>
 struct Ops {
   static constexpr int KB = D / 32, KTW = D / 64;
   HFrag w[KB];           // W, token tile of this wave
   HFrag qp[KB];          // Q', token tile of this wave
   HFrag kc[KTW][2];      // Kc^T for this wave's key tiles
-  HHalf u, bu;           // U and Bqk U, token tile of this wave, this slice
+  HHalf u[VT], bu[VT];   // U and Bqk U, token tile of this wave, the slice's value tiles
   f32x4 gam[KTW];        // e^G[C-1] for this lane's key rows
 };
 
 // The operand loads of one chunk, in three parts that the step spreads over
 // its phases so that the vector memory path works while the MFMAs do.
-template <int D>
-__device__ __forceinline__ void load_ops_part(Ops<D>& o, const unsigned char* __restrict__ rec, int part, int w,
-                                              int l, int g, int vt) {
+template <int D, int VT>
+__device__ __forceinline__ void load_ops_part(Ops<D, VT>& o, const unsigned char* __restrict__ rec, int part,
+                                              int w, int l, int g, int vt0) {
   using R = Rec<D>;
-  using O = Ops<D>;
+  using O = Ops<D, VT>;
   if (part == 0) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
       o.w[p] = *reinterpret_cast<const HFrag*>(rec + R::W + ((w * O::KB + p) * 64 + l) * 16);
-    o.u = *reinterpret_cast<const HHalf*>(rec + R::U + ((vt * 4 + w) * 64 + l) * 8);
-    o.bu = *reinterpret_cast<const HHalf*>(rec + R::BU + ((vt * 4 + w) * 64 + l) * 8);
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      o.u[t] = *reinterpret_cast<const HHalf*>(rec + R::U + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+      o.bu[t] = *reinterpret_cast<const HHalf*>(rec + R::BU + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+    }
   } else if (part == 1) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p)
@@ -586,23 +591,22 @@ __device__ __forceinline__ void load_ops_part(Ops<D>& o, const unsigned char* __
   }
 }
 
-template <int D>
-__device__ __forceinline__ void load_ops(Ops<D>& o, const unsigned char* __restrict__ rec, int w, int l, int g,
-                                         int vt) {
+template <int D, int VT>
+__device__ __forceinline__ void load_ops(Ops<D, VT>& o, const unsigned char* __restrict__ rec, int w, int l, int g,
+                                         int vt0) {
 #pragma unroll
-  for (int part = 0; part < 3; ++part) load_ops_part<D>(o, rec, part, w, l, g, vt);
+  for (int part = 0; part < 3; ++part) load_ops_part<D, VT>(o, rec, part, w, l, g, vt0);
 }
 
 // One workgroup per CU: the pass is bound by the operand bytes a CU keeps in
 // flight, and a second workgroup on the same CU lowers the throughput of
 // both (variable-length batches with more workgroups than CUs).
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(const int32_t* __restrict__ cu, int N, int H,
-                                                         const float* init, float* fin, In* __restrict__ o,
-                                                         const unsigned char* __restrict__ ws,
-                                                         const int32_t* __restrict__ sidx, int pool_slots) {
+template <int D, int VT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(
+    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin, In* __restrict__ o,
+    const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx, int pool_slots) {
   using R = Rec<D>;
-  constexpr int NV = D / 16, KB = D / 32, KTW = D / 64;
+  constexpr int NV = D / (16 * VT), KB = D / 32, KTW = D / 64;
 
   // XCD-aware order: the NV slices of one (sequence, head) share an XCD (and
   // its L2) because workgroups are dealt to the 8 XCDs round-robin.
@@ -615,74 +619,90 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
-  const int col = 16 * vt + l16;
+  const int vt0 = vt * VT;   // first value tile of the slice
   const int64_t bos = cu[n], eos = cu[n + 1];
   const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = bos / kChunk + n;
 
-  __shared__ HFrag sS[KB][64];   // S as the B operand
-  __shared__ HFrag sE[2][64];    // E as the B operand
+  __shared__ HFrag sS[VT][KB][64];   // S as the B operand
+  __shared__ HFrag sE[VT][2][64];    // E as the B operand
 
   const int64_t sslot = state_slot(sidx, pool_slots, n);
   if (sslot < 0) init = nullptr, fin = nullptr;
   const int64_t sbase = (sslot * H + h) * D;   // row (value channel) base of state[slot][h]
-  f32x4 S[KTW];
+  f32x4 S[VT][KTW];
 #pragma unroll
-  for (int kt = 0; kt < KTW; ++kt) {
-    const int kti = w * KTW + kt;
-    S[kt] = init ? *reinterpret_cast<const f32x4*>(init + (sbase + col) * D + 16 * kti + 4 * g)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < VT; ++t)
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int kti = w * KTW + kt, col = 16 * (vt0 + t) + l16;
+      S[t][kt] = init ? *reinterpret_cast<const f32x4*>(init + (sbase + col) * D + 16 * kti + 4 * g)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES; };
 
   // one chunk step with operands `ops`; meanwhile the operands of a later
   // chunk (record `nrec`) are loaded into `nxt`, one part per phase
-  auto step = [&](const Ops<D>& ops, int c, Ops<D>& nxt, const unsigned char* nrec) {
-    load_ops_part<D>(nxt, nrec, 0, w, l, g, vt);
+  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, const unsigned char* nrec) {
+    load_ops_part<D, VT>(nxt, nrec, 0, w, l, g, vt0);
     const int64_t t0 = bos + (int64_t)c * kChunk;
     const int len = (int)min<int64_t>(kChunk, eos - t0);
 #pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      const int kti = w * KTW + kt;
-      HHalf hs;
+    for (int t = 0; t < VT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hs[e] = (_Float16)S[kt][e];
-      *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sS[kti >> 1][l]) + 4 * (kti & 1)) = hs;
-    }
+      for (int kt = 0; kt < KTW; ++kt) {
+        const int kti = w * KTW + kt;
+        HHalf hs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs[e] = (_Float16)S[t][kt][e];
+        *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sS[t][kti >> 1][l]) + 4 * (kti & 1)) = hs;
+      }
     __syncthreads();
-    load_ops_part<D>(nxt, nrec, 1, w, l, g, vt);
+    load_ops_part<D, VT>(nxt, nrec, 1, w, l, g, vt0);
     // token tile w: W S first -- E gates the other waves; Q' S only after
     // the state update has been issued
-    HFrag sf[KB];
+    HFrag sf[VT][KB];
 #pragma unroll
-    for (int p = 0; p < KB; ++p) sf[p] = sS[p][l];
-    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum;
+    for (int t = 0; t < VT; ++t)
 #pragma unroll
-    for (int p = 0; p < KB; ++p) mma(wsum, ops.w[p], sf[p]);
-    // E = U - W S, published as the B operand over tokens
-    HHalf eh;
+      for (int p = 0; p < KB; ++p) sf[t][p] = sS[t][p][l];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) eh[e] = (_Float16)((float)ops.u[e] - wsum[e]);
-    *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[w >> 1][l]) + 4 * (w & 1)) = eh;
+    for (int t = 0; t < VT; ++t) {
+      f32x4 wsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < KB; ++p) mma(wsum, ops.w[p], sf[t][p]);
+      // E = U - W S, published as the B operand over tokens
+      HHalf eh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eh[e] = (_Float16)((float)ops.u[t][e] - wsum[e]);
+      *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[t][w >> 1][l]) + 4 * (w & 1)) = eh;
+    }
     __syncthreads();
-    load_ops_part<D>(nxt, nrec, 2, w, l, g, vt);
+    load_ops_part<D, VT>(nxt, nrec, 2, w, l, g, vt0);
     // S <- Diag(e^G[C-1]) S + Kc^T E
 #pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      S[kt] *= ops.gam[kt];
+    for (int t = 0; t < VT; ++t)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) mma(S[kt], ops.kc[kt][p], sE[p][l]);
-    }
+      for (int kt = 0; kt < KTW; ++kt) {
+        S[t][kt] *= ops.gam[kt];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) mma(S[t][kt], ops.kc[kt][p], sE[t][p][l]);
+      }
     // O = Q' S + Bqk U for token tile w: off the state's dependency chain
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[e];
+    for (int t = 0; t < VT; ++t) {
+      f32x4 qsum;
 #pragma unroll
-    for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[p]);
+      for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[t][e];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * g + e;
-      if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
+      for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[t][p]);
+      const int col = 16 * (vt0 + t) + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * g + e;
+        if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
+      }
     }
   };
 
@@ -692,10 +712,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // loads and the compiler's waits stay exact).  Twelve steps per loop
   // iteration: at the loop head the compiler waits for most loads in flight,
   // so the head is reached once every twelve chunks rather than every three.
-  Ops<D> bufA, bufB, bufC;
+  Ops<D, VT> bufA, bufB, bufC;
   if (nch > 0) {
-    load_ops<D>(bufA, rec_of(0), w, l, g, vt);
-    load_ops<D>(bufB, rec_of(1), w, l, g, vt);
+    load_ops<D, VT>(bufA, rec_of(0), w, l, g, vt0);
+    load_ops<D, VT>(bufB, rec_of(1), w, l, g, vt0);
   }
   for (int c0 = 0; c0 < nch; c0 += 12) {
 #pragma unroll
@@ -712,10 +732,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   if (fin) {
 #pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) {
-      const int kti = w * KTW + kt;
-      *reinterpret_cast<f32x4*>(fin + (sbase + col) * D + 16 * kti + 4 * g) = S[kt];
-    }
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt) {
+        const int kti = w * KTW + kt, col = 16 * (vt0 + t) + l16;
+        *reinterpret_cast<f32x4*>(fin + (sbase + col) * D + 16 * kti + 4 * g) = S[t][kt];
+      }
   }
 }
 
@@ -732,12 +754,22 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // Slices of one value tile while they fit the CUs in one round: each
+  // chunk step is then shortest.  With more slices than CUs the pass is
+  // bound by throughput, and slices of two value tiles, which load W, Q'
+  // and Kc once for both, do the same work with fewer operand bytes
+  // (the results are the same bit for bit).
   const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
   const int64_t groups = (pairs + 7) / 8;
-  const unsigned blocks = (unsigned)(groups * 8 * (D / 16));
-  hipLaunchKernelGGL((state_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
-                     A.num_heads, A.init_state, A.final_state, (In*)A.o, (const unsigned char*)A.workspace,
-                     A.state_indices, A.pool_slots);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const bool wide = pairs * (D / 16) > cus;
+  const unsigned blocks = (unsigned)(groups * 8 * (D / (wide ? 32 : 16)));
+  auto kern = wide ? state_kernel<D, 2> : state_kernel<D, 1>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs, A.num_heads,
+                     A.init_state, A.final_state, (In*)A.o, (const unsigned char*)A.workspace, A.state_indices,
+                     A.pool_slots);
   return hipGetLastError();
 }
 

@@ -23,7 +23,10 @@
  *   buffers, 16-byte aligned, owned by the caller.  The library allocates
  *   nothing, copies nothing between host and device, never synchronises and
  *   keeps no global mutable state; it only enqueues kernels on `stream`
- *   (0 = the null stream).  Buffers must stay valid until that work is done.
+ *   (0 = the null stream), after reading the current device's compute-unit
+ *   count, which picks the launch shape of the bf16 prefill's state pass
+ *   (the results are the same bit for bit either way).  Buffers must stay
+ *   valid until that work is done.
  * - log_alpha is the natural logarithm of the decay gate alpha (fp32, <= 0):
  *   alpha_t[i] in (0, 1) decays key channel i (the per-channel gate of the
  *   "Kimi Linear Guide" page, section "2. Channel-Wise Data-Dependent

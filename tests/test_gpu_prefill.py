@@ -69,11 +69,14 @@ def test_ragged_varlen(dtype, D):
     check(d, TOL[dtype], f"ragged varlen {dtype} D={D}")
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64), (torch.bfloat16, 64)],
+                         ids=["bf16-128", "f32-64", "bf16-64"])
 def test_many_short_sequences(dtype, D):
     """257 sequences (more than the CUs, not a multiple of the 8-way block
     interleave) of seeded lengths 0..150 over H = 5 heads: the chunk-slot map
-    and the block order of both kernels at scale"""
+    and the block order of both kernels at scale, and (bf16) the state pass
+    with two value tiles per workgroup, chosen when the slices outnumber the
+    CUs"""
     lengths = np.random.default_rng(470 + D).integers(0, 151, size=257).tolist()
     lengths[0], lengths[-1] = 0, 64   # an empty first and an exact-chunk last sequence
     d = make_case(lengths, H=5, D=D, dtype=dtype, seed=471 + D)
