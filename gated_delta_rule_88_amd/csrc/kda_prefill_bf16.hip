@@ -756,17 +756,18 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   }
   // Slices of one value tile while they fit the CUs in one round: each
   // chunk step is then shortest.  With more slices than CUs the pass is
-  // bound by throughput, and slices of two value tiles, which load W, Q'
-  // and Kc once for both, do the same work with fewer operand bytes
+  // bound by throughput, and slices of two or four value tiles, which load
+  // W, Q' and Kc once for all their columns, do the same work with fewer
+  // operand bytes: the widest slice that still gives every CU a workgroup
   // (the results are the same bit for bit).
   const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
   const int64_t groups = (pairs + 7) / 8;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const bool wide = pairs * (D / 16) > cus;
-  const unsigned blocks = (unsigned)(groups * 8 * (D / (wide ? 32 : 16)));
-  auto kern = wide ? state_kernel<D, 2> : state_kernel<D, 1>;
+  const int vt = pairs * (D / 64) >= cus ? 4 : pairs * (D / 32) >= cus ? 2 : 1;
+  const unsigned blocks = (unsigned)(groups * 8 * (D / (16 * vt)));
+  auto kern = vt == 4 ? state_kernel<D, 4> : vt == 2 ? state_kernel<D, 2> : state_kernel<D, 1>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs, A.num_heads,
                      A.init_state, A.final_state, (In*)A.o, (const unsigned char*)A.workspace, A.state_indices,
                      A.pool_slots);

@@ -83,6 +83,16 @@ def test_many_short_sequences(dtype, D):
     check(d, TOL[dtype], f"257 short sequences {dtype} D={D}")
 
 
+@pytest.mark.parametrize("nseq,H", [(7, 3), (20, 4), (75, 4)], ids=["1-tile", "2-tile", "4-tile"])
+def test_state_pass_slice_widths(nseq, H):
+    """the bf16 state pass takes slices of 1, 2 or 4 value tiles depending on
+    how many (sequence, head) pairs there are against the CUs (21, 80 and 300
+    pairs here, on a 256-CU device); every width must match the oracle"""
+    lengths = np.random.default_rng(490 + nseq).integers(1, 200, size=nseq).tolist()
+    d = make_case(lengths, H=H, D=128, dtype=torch.bfloat16, seed=491 + nseq)
+    check(d, TOL[torch.bfloat16], f"state pass slice width, {nseq} x {H} pairs")
+
+
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
 def test_chunk_counts_around_the_loop_unroll(dtype, D):
     """sequences of 11, 12, 13, 24 and 25 chunks (full and partial last
