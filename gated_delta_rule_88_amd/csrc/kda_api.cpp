@@ -93,8 +93,16 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
   if (check_common(num_seqs, num_heads, dk, dv, dtype) != KDA_OK) return 0;
   if (total_tokens < 0 || total_tokens > INT32_MAX) return 0;
   const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
-  const size_t rec = dtype == KDA_BF16 ? kda::prefill_record_bytes_bf16(dk) : kda::prefill_record_bytes_f32(dk);
-  return (size_t)slots * (size_t)num_heads * rec;
+  if (dtype == KDA_BF16) return kda::prefill_workspace_bytes_bf16(slots, num_heads, dk);
+  return kda::prefill_status_offset_f32(slots, num_heads, dk) + 16;
+}
+
+size_t kda_prefill_status_offset(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk,
+                                 int32_t dv, kda_dtype dtype) {
+  if (kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) == 0) return SIZE_MAX;
+  const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
+  return dtype == KDA_BF16 ? kda::prefill_status_offset_bf16(slots, num_heads, dk)
+                           : kda::prefill_status_offset_f32(slots, num_heads, dk);
 }
 
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,

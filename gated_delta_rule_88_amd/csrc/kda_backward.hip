@@ -616,8 +616,10 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict__ cu, int N, int H,
-                                                       const float* __restrict__ grad_final,
-                                                       float* __restrict__ grad_init, float* __restrict__ ws) {
+                                                       const float* grad_final, float* grad_init,
+                                                       float* __restrict__ ws) {
+  // grad_init may be the grad_final buffer (in-place): each element is read
+  // before the same thread writes it, so the two are not declared restrict
   using L = Ws<D>;
   // LDS strides chosen so that every MFMA operand read is conflict-free:
   // Bq is read over (token, s) pairs, Kc over (token, key), Qg and W over

@@ -62,6 +62,14 @@ struct BackwardArgs {
 // and the number of chunk slots reserved for (num_seqs, total_tokens).
 size_t prefill_record_bytes_f32(int d);
 size_t prefill_record_bytes_bf16(int d);
+// Whole workspace of the bf16 path: records, chunk-ready flags and a header;
+// the byte offset of the call's status word in it.
+size_t prefill_workspace_bytes_bf16(int64_t slots, int num_heads, int d);
+size_t prefill_status_offset_bf16(int64_t slots, int num_heads, int d);
+// fp32 path: records, then the status word (16-byte aligned, 16 bytes).
+size_t prefill_status_offset_f32(int64_t slots, int num_heads, int d);
+// Enqueues a kernel that sets *status to 0.
+hipError_t clear_prefill_status(int* status, hipStream_t stream);
 int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -41,28 +41,32 @@
 namespace kda {
 
 // ---------------------------------------------------------------------------
-// Per (chunk slot, head) record in the workspace.  Operands whose rounding
-// to bf16 would show in the outputs are stored as a hi + lo pair (NS = 2):
-// Qg and S meet in the read-out Qg S0, where the result is often much
-// smaller than the terms; Kc feeds the state, which carries its error to
-// every later token; Bqk multiplies E in the intra-chunk read-out.  W enters
-// only through E and stays single.
+// Per (chunk slot, head) record in the workspace: the state pass's operands
+// as fp32 MFMA fragments.
 // ---------------------------------------------------------------------------
-template <class P, int D>
+template <int D>
 struct Rec {
-  static constexpr int ES = sizeof(typename P::In);
-  static constexpr int NS = P::kSplit ? 2 : 1;      // stored parts (hi, lo)
   static constexpr int KB = D / 32;                 // 32-deep key blocks
   static constexpr int NT = D / 16;                 // 16-wide key / value tiles
-  static constexpr size_t FB = 64 * 8 * ES;         // bytes per fragment
+  static constexpr size_t FB = 64 * 8 * 4;          // bytes per fragment
   static constexpr size_t W = 0;                       // [4 token tiles][KB]       W    (row token, k key)
-  static constexpr size_t Q = W + 4 * KB * FB;         // [NS][4][KB]               Qg   (row token, k key)
-  static constexpr size_t KC = Q + NS * 4 * KB * FB;   // [NS][NT key tiles][2]     Kc^T (row key, k token)
-  static constexpr size_t B = KC + NS * NT * 2 * FB;   // [NS][4 token tiles][2]    Bqk  (row token, k token)
-  static constexpr size_t U = B + NS * 8 * FB;         // [NT value tiles][4 token tiles][64] f32x4
+  static constexpr size_t Q = W + 4 * KB * FB;         // [4][KB]                   Qg   (row token, k key)
+  static constexpr size_t KC = Q + 4 * KB * FB;        // [NT key tiles][2]         Kc^T (row key, k token)
+  static constexpr size_t B = KC + NT * 2 * FB;        // [4 token tiles][2]        Bqk  (row token, k token)
+  static constexpr size_t U = B + 8 * FB;              // [NT value tiles][4 token tiles][64] f32x4
   static constexpr size_t G = U + (size_t)NT * 4 * 64 * 16;  // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
+
+using Frag = f32x8;
+using Half = f32x4;
+
+__device__ __forceinline__ Frag frag8(const float (&v)[8]) {
+  Frag f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) f[m] = v[m];
+  return f;
+}
 
 // Chunk slots: chunk c of sequence n lives in slot cu[n]/64 + n + c.  Slots
 // of different sequences never collide (floor(a/64) + ceil(L/64) <=
@@ -71,8 +75,11 @@ int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens) {
   return total_tokens / kChunk + num_seqs + 1;
 }
 
-size_t prefill_record_bytes_f32(int d) {
-  return d == 128 ? Rec<PathF32, 128>::BYTES : Rec<PathF32, 64>::BYTES;
+size_t prefill_record_bytes_f32(int d) { return d == 128 ? Rec<128>::BYTES : Rec<64>::BYTES; }
+
+// The status word follows the records.
+size_t prefill_status_offset_f32(int64_t slots, int num_heads, int d) {
+  return (size_t)slots * num_heads * prefill_record_bytes_f32(d);
 }
 
 // ---------------------------------------------------------------------------
@@ -80,16 +87,13 @@ size_t prefill_record_bytes_f32(int d) {
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512;
 
-template <class P, int D>
+template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
-    const typename P::In* __restrict__ q, const typename P::In* __restrict__ k,
-    const typename P::In* __restrict__ v, const float* __restrict__ log_alpha,
-    const typename P::In* __restrict__ beta, const int32_t* __restrict__ cu, int N, int H,
-    unsigned char* __restrict__ ws, int scalar_gate, int raw_qkb) {
-  using In = typename P::In;
-  using Frag = typename P::Frag;
-  using Half = typename P::Half;
-  using R = Rec<P, D>;
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta, const int32_t* __restrict__ cu, int N,
+    int H, unsigned char* __restrict__ ws, int scalar_gate, int raw_qkb, int* __restrict__ status) {
+  using In = float;
+  using R = Rec<D>;
   constexpr int C = kChunk;
   constexpr int NTH = kPrepThreads;
   constexpr int NW = NTH / 64;                       // waves
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
       *reinterpret_cast<uint4*>(&sQ[r][cv * EV]) = qq;
     }
     if (tid < C) {
-      const float b = tid < len ? to_f32(beta[(t0 + tid) * H + h]) : 0.f;
+      const float b = tid < len ? beta[(t0 + tid) * H + h] : 0.f;
       sBeta[tid] = (raw_qkb && tid < len) ? sigmoid(b) : b;
     }
     for (int idx = tid; idx < C * PL; idx += NTH) (&sL[0][0])[idx] = 0.f;
@@ -148,14 +152,14 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
       const int r = tid % C;
       const In* row = tid < C ? &sK[r][0] : &sQ[r][0];
       float ss = 0.f;
-      for (int i = 0; i < D; ++i) ss += to_f32(row[i]) * to_f32(row[i]);
+      for (int i = 0; i < D; ++i) ss += row[i] * row[i];
       sNrm[tid / C][r] = inv_norm(ss);
     }
     __syncthreads();
     for (int idx = tid; idx < C * D; idx += NTH) {
       const int r = idx / D, i = idx % D;
-      sK[r][i] = from_f32<In>(to_f32(sK[r][i]) * sNrm[0][r]);
-      sQ[r][i] = from_f32<In>(to_f32(sQ[r][i]) * sNrm[1][r]);
+      sK[r][i] *= sNrm[0][r];
+      sQ[r][i] *= sNrm[1][r];
     }
     __syncthreads();
   }
@@ -186,8 +190,16 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     if (s == SEGS - 1) sGc[i] = gl[SL - 1];
     __syncthreads();
     const float gm = sGm[i], gc = sGc[i];
+    float dgmax = 0.f;
 #pragma unroll
-    for (int r = 0; r < SL; ++r) sX[s * SL + r][i] = __expf(gl[r] - gm);
+    for (int r = 0; r < SL; ++r) {
+      sX[s * SL + r][i] = __expf(gl[r] - gm);
+      dgmax = fmaxf(dgmax, fabsf(gl[r] - gm));
+    }
+    // a gate sum beyond the fp32 exponent range: report it (results of this
+    // chunk may be non-finite)
+    if (__any(dgmax > kMaxAnchoredExp) && l == 0)
+      __hip_atomic_fetch_or(status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (s == 0) {
       sEgm[i] = __expf(gm);
       sEcm[i] = __expf(gc - gm);
@@ -220,9 +232,9 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
         row_frag(sK, 16 * rt + l16, p, false, va);   // Ka: k_r e^(G_r - G_m)
         row_frag(sK, 16 * jt + l16, p, true, vb);    // Kbar: k_j e^(G_m - G_j)
         row_frag(sQ, 16 * rt + l16, p, false, vq);   // Qa: q_r e^(G_r - G_m)
-        const Split<P> ka = make_split<P>(va), kb = make_split<P>(vb), qa = make_split<P>(vq);
-        mma_ss<P>(accA, ka, kb);   // A[r][j]
-        mma_ss<P>(accB, kb, qa);   // Bqk^T[j][r]
+        const Frag ka = frag8(va), kb = frag8(vb), qa = frag8(vq);
+        mma(accA, ka, kb);   // A[r][j]
+        mma(accB, kb, qa);   // Bqk^T[j][r]
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -230,36 +242,28 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
         sL[r][j] = (j < r) ? sBeta[r] * accA[e] : 0.f;
       }
       // Bqk fragment (row tile rt, token block jt/2): lane l holds row
-      // r = 16 rt + l16 and columns j = 16 jt + 4 g + e, as hi and lo
-      Half hb, lb;
+      // r = 16 rt + l16 and columns j = 16 jt + 4 g + e
+      Half hb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 16 * jt + 4 * g + e, r = 16 * rt + l16;
-        const float x = j <= r ? accB[e] : 0.f;
-        hb[e] = from_f32<In>(x);
-        lb[e] = from_f32<In>(x - to_f32(hb[e]));
+        hb[e] = j <= r ? accB[e] : 0.f;
       }
       const size_t foff = ((size_t)(rt * 2 + jt / 2) * 64 + l) * FS + 4 * (jt & 1) * sizeof(In);
       *reinterpret_cast<Half*>(rec + R::B + foff) = hb;
-      if constexpr (P::kSplit) *reinterpret_cast<Half*>(rec + R::B + 8 * R::FB + foff) = lb;
       if (jt == rt && (rt & 1) == 0) {   // columns above the diagonal block
-        Half z;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = from_f32<In>(0.f);
         const size_t zoff = ((size_t)(rt * 2 + jt / 2) * 64 + l) * FS + 4 * sizeof(In);
-        *reinterpret_cast<Half*>(rec + R::B + zoff) = z;
-        if constexpr (P::kSplit) *reinterpret_cast<Half*>(rec + R::B + 8 * R::FB + zoff) = z;
+        *reinterpret_cast<Half*>(rec + R::B + zoff) = Half{0.f, 0.f, 0.f, 0.f};
       }
     }
-    // Qg fragments (token tile rt, key block p), hi and lo
+    // Qg fragments (token tile rt, key block p)
     for (int f = w; f < 4 * KB; f += NW) {
       const int rt = f / KB, p = f % KB;
       float vq[8];
       row_frag(sQ, 16 * rt + l16, p, false, vq);
 #pragma unroll
       for (int m = 0; m < 8; ++m) vq[m] *= sEgm[32 * p + kpos(g, m)];
-      store_split<P>(rec + R::Q, rec + R::Q + 4 * KB * R::FB, ((size_t)f * 64 + l) * FS,
-                     make_split<P>(vq));
+      *reinterpret_cast<Frag*>(rec + R::Q + ((size_t)f * 64 + l) * FS) = frag8(vq);
     }
   }
   __syncthreads();   // Q is dead from here on: its space becomes T
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
   {
     // T' fragments (row tile rt, token block p): the B operand of W^T and
     // the A operand of U (the two layouts coincide)
-    Split<P> tf[4][2];
+    Frag tf[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -357,28 +361,27 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
           const int j = 32 * p + kpos(g, m);
           vals[m] = sT[16 * rt + l16][j] * sBeta[j];
         }
-        tf[rt][p] = make_split<P>(vals);
+        tf[rt][p] = frag8(vals);
       }
     // tasks 0..NT-1: key tile (W, Kc); NT..2NT-1: value tile (U)
     for (int task = w; task < 2 * NT; task += NW) {
       if (task < NT) {
         const int it = task;
         const int col = 16 * it + l16;   // key channel of this lane
-        Split<P> kg[2];
+        Frag kg[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           float vg[8], vc[8];
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             const int j = 32 * p + kpos(g, m);
-            const float kx = to_f32(sK[j][col]);
+            const float kx = sK[j][col];
             const float x = sX[j][col];
             vg[m] = kx * x * sEgm[col];
             vc[m] = kx * __builtin_amdgcn_rcpf(x) * sEcm[col];
           }
-          kg[p] = make_split<P>(vg);
-          store_split<P>(rec + R::KC, rec + R::KC + NT * 2 * R::FB,
-                         ((size_t)(it * 2 + p) * 64 + l) * FS, make_split<P>(vc));
+          kg[p] = frag8(vg);
+          *reinterpret_cast<Frag*>(rec + R::KC + ((size_t)(it * 2 + p) * 64 + l) * FS) = frag8(vc);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -386,13 +389,10 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             if (p > (rt >> 1)) break;   // T'[r][j] = 0 for j > r
-            mma_ss<P>(accW, kg[p], tf[rt][p]);
+            mma(accW, kg[p], tf[rt][p]);
           }
-          Half hw;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hw[e] = from_f32<In>(accW[e]);
           const size_t off = ((size_t)(rt * KB + it / 2) * 64 + l) * FS + 4 * (it & 1) * sizeof(In);
-          *reinterpret_cast<Half*>(rec + R::W + off) = hw;
+          *reinterpret_cast<Half*>(rec + R::W + off) = accW;
         }
       } else {
         const int ct = task - NT;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             const int j = 32 * p + kpos(g, m);
-            vf[p][m] = j < len ? v[((t0 + j) * H + h) * D + col] : from_f32<In>(0.f);
+            vf[p][m] = j < len ? v[((t0 + j) * H + h) * D + col] : 0.f;
           }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             if (p > (rt >> 1)) break;
-            mma_sx<P>(accU, tf[rt][p], vf[p]);
+            mma(accU, tf[rt][p], vf[p]);
           }
           *reinterpret_cast<f32x4*>(rec + R::U + ((size_t)(ct * 4 + rt) * 64 + l) * 16) = accU;
         }
@@ -426,67 +426,53 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
 // slice as accumulators and token tile w of every chunk.  The operands of
 // chunk c+1 are loaded into registers while chunk c is computed.
 // ---------------------------------------------------------------------------
-template <class P, int D>
+template <int D>
 struct ChunkOps {
-  using Frag = typename P::Frag;
-  static constexpr int KB = D / 32, KTW = D / 64, NS = P::kSplit ? 2 : 1;
+  static constexpr int KB = D / 32, KTW = D / 64;
   Frag w[KB];          // W, token tile of this wave
-  Frag q[NS][KB];      // Qg hi/lo
-  Frag kc[NS][KTW][2]; // Kc^T hi/lo, key tiles of this wave
-  Frag b[NS][2];       // Bqk hi/lo
+  Frag q[KB];          // Qg
+  Frag kc[KTW][2];     // Kc^T, key tiles of this wave
+  Frag b[2];           // Bqk
   f32x4 u;             // U, token tile of this wave, this value slice
   f32x4 gam[KTW];      // e^G[C-1] for this lane's key rows
 };
 
-template <class P, int D>
-__device__ __forceinline__ void load_ops(ChunkOps<P, D>& o, const unsigned char* __restrict__ rec,
-                                         int w, int l, int g, int vt) {
-  using Frag = typename P::Frag;
-  using R = Rec<P, D>;
-  using O = ChunkOps<P, D>;
+template <int D>
+__device__ __forceinline__ void load_ops(ChunkOps<D>& o, const unsigned char* __restrict__ rec, int w, int l, int g,
+                                         int vt) {
+  using R = Rec<D>;
+  using O = ChunkOps<D>;
   constexpr size_t FS = sizeof(Frag);
 #pragma unroll
   for (int p = 0; p < O::KB; ++p)
     o.w[p] = *reinterpret_cast<const Frag*>(rec + R::W + ((size_t)(w * O::KB + p) * 64 + l) * FS);
 #pragma unroll
-  for (int s = 0; s < O::NS; ++s)
+  for (int p = 0; p < O::KB; ++p)
+    o.q[p] = *reinterpret_cast<const Frag*>(rec + R::Q + ((size_t)(w * O::KB + p) * 64 + l) * FS);
 #pragma unroll
-    for (int p = 0; p < O::KB; ++p)
-      o.q[s][p] = *reinterpret_cast<const Frag*>(rec + R::Q + ((size_t)((s * 4 + w) * O::KB + p) * 64 + l) * FS);
+  for (int kt = 0; kt < O::KTW; ++kt)
 #pragma unroll
-  for (int s = 0; s < O::NS; ++s)
-#pragma unroll
-    for (int kt = 0; kt < O::KTW; ++kt)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int kti = w * O::KTW + kt;
-        o.kc[s][kt][p] = *reinterpret_cast<const Frag*>(
-            rec + R::KC + ((size_t)((s * R::NT + kti) * 2 + p) * 64 + l) * FS);
-      }
+    for (int p = 0; p < 2; ++p) {
+      const int kti = w * O::KTW + kt;
+      o.kc[kt][p] = *reinterpret_cast<const Frag*>(rec + R::KC + ((size_t)(kti * 2 + p) * 64 + l) * FS);
+    }
   // both token blocks of Bqk are loaded (the second is unused for w < 2) so
   // that every chunk issues the same loads and the waits stay exact
 #pragma unroll
-  for (int s = 0; s < O::NS; ++s)
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      o.b[s][p] = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)((s * 4 + w) * 2 + p) * 64 + l) * FS);
+  for (int p = 0; p < 2; ++p)
+    o.b[p] = *reinterpret_cast<const Frag*>(rec + R::B + ((size_t)(w * 2 + p) * 64 + l) * FS);
   o.u = *reinterpret_cast<const f32x4*>(rec + R::U + ((size_t)(vt * 4 + w) * 64 + l) * 16);
 #pragma unroll
   for (int kt = 0; kt < O::KTW; ++kt)
     o.gam[kt] = *reinterpret_cast<const f32x4*>(rec + R::G + (size_t)(16 * (w * O::KTW + kt) + 4 * g) * 4);
 }
 
-template <class P, int D>
+template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
-    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin,
-    typename P::In* __restrict__ o, const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx,
-    int pool_slots) {
-  using In = typename P::In;
-  using Frag = typename P::Frag;
-  using Half = typename P::Half;
-  using R = Rec<P, D>;
+    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin, float* __restrict__ o,
+    const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx, int pool_slots) {
+  using R = Rec<D>;
   constexpr int NV = D / 16, KB = D / 32, KTW = D / 64;
-  constexpr int NS = P::kSplit ? 2 : 1;
 
   // XCD-aware order: the NV slices of one (sequence, head) share an XCD (and
   // its L2) because workgroups are dealt to the 8 XCDs round-robin.
@@ -504,8 +490,8 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = bos / kChunk + n;
 
-  __shared__ Frag sS[NS][KB][64];   // S as the B operand, hi/lo
-  __shared__ Frag sE[NS][2][64];    // E as the B operand, hi/lo
+  __shared__ Frag sS[KB][64];   // S as the B operand
+  __shared__ Frag sE[2][64];    // E as the B operand
 
   const int64_t sslot = state_slot(sidx, pool_slots, n);
   if (sslot < 0) init = nullptr, fin = nullptr;
@@ -521,95 +507,61 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES; };
 
   // one chunk step with operands `ops`
-  auto step = [&](const ChunkOps<P, D>& ops, int c) {
-      const int64_t t0 = bos + (int64_t)c * kChunk;
-      const int len = (int)min<int64_t>(kChunk, eos - t0);
+  auto step = [&](const ChunkOps<D>& ops, int c) {
+    const int64_t t0 = bos + (int64_t)c * kChunk;
+    const int len = (int)min<int64_t>(kChunk, eos - t0);
 
-      // S as the B operand (reduction over keys), hi and lo
-  #pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) {
-        const int kti = w * KTW + kt;
-        Half hs, ls;
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hs[e] = from_f32<In>(S[kt][e]);
-          ls[e] = from_f32<In>(S[kt][e] - to_f32(hs[e]));
-        }
-        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[0][kti >> 1][l]) + 4 * (kti & 1)) = hs;
-        if constexpr (P::kSplit)
-          *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sS[1][kti >> 1][l]) + 4 * (kti & 1)) = ls;
-      }
-      __syncthreads();
+    // S as the B operand (reduction over keys)
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int kti = w * KTW + kt;
+      *reinterpret_cast<Half*>(reinterpret_cast<float*>(&sS[kti >> 1][l]) + 4 * (kti & 1)) = S[kt];
+    }
+    __syncthreads();
 
-      // token tile w: W S0 (hi only: it only enters through E) and Qg S0 (split)
-      f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-      for (int p = 0; p < KB; ++p) {
-        const Frag sh = sS[0][p][l];
-        mma(wsum, ops.w[p], sh);
-        mma(qsum, ops.q[0][p], sh);
-        if constexpr (P::kSplit) {
-          const Frag sl = sS[1][p][l];
-          mma(qsum, ops.q[0][p], sl);
-          mma(qsum, ops.q[1][p], sh);
-        }
-      }
-      // E = U - W S0 for token tile w, published split as the B operand of
-      // the reductions over tokens
-      Half eh, el;
-  #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ev = ops.u[e] - wsum[e];
-        eh[e] = from_f32<In>(ev);
-        el[e] = from_f32<In>(ev - to_f32(eh[e]));
-      }
-      *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[0][w >> 1][l]) + 4 * (w & 1)) = eh;
-      if constexpr (P::kSplit)
-        *reinterpret_cast<Half*>(reinterpret_cast<In*>(&sE[1][w >> 1][l]) + 4 * (w & 1)) = el;
-      __syncthreads();
+    // token tile w: W S0 and Qg S0
+    f32x4 wsum = {0.f, 0.f, 0.f, 0.f}, qsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      const Frag sh = sS[p][l];
+      mma(wsum, ops.w[p], sh);
+      mma(qsum, ops.q[p], sh);
+    }
+    // E = U - W S0 for token tile w, published as the B operand of the
+    // reductions over tokens
+    *reinterpret_cast<Half*>(reinterpret_cast<float*>(&sE[w >> 1][l]) + 4 * (w & 1)) = ops.u - wsum;
+    __syncthreads();
 
-      // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
-  #pragma unroll
-      for (int kt = 0; kt < KTW; ++kt) {
-        S[kt] *= ops.gam[kt];
-  #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const Frag eh2 = sE[0][p][l];
-          mma(S[kt], ops.kc[0][kt][p], eh2);
-          if constexpr (P::kSplit) {
-            mma(S[kt], ops.kc[0][kt][p], sE[1][p][l]);
-            mma(S[kt], ops.kc[1][kt][p], eh2);
-          }
-        }
-      }
-      // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
-  #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if (p > (w >> 1)) break;
-        const Frag eh2 = sE[0][p][l];
-        mma(qsum, ops.b[0][p], eh2);
-        if constexpr (P::kSplit) {
-          mma(qsum, ops.b[0][p], sE[1][p][l]);
-          mma(qsum, ops.b[1][p], eh2);
-        }
-      }
-  #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * g + e;
-        if (r < len) o[((t0 + r) * H + h) * D + col] = from_f32<In>(qsum[e]);
-      }
+    // S <- Diag(e^G[C-1]) S + Kc^T E  (this wave's key tiles)
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      S[kt] *= ops.gam[kt];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) mma(S[kt], ops.kc[kt][p], sE[p][l]);
+    }
+    // O = Qg S0 + Bqk E for token tile w (token blocks p <= w/2)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p > (w >> 1)) break;
+      mma(qsum, ops.b[p], sE[p][l]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * g + e;
+      if (r < len) o[((t0 + r) * H + h) * D + col] = qsum[e];
+    }
   };
 
   // ping-pong buffers: the loads for chunk c+1 are in flight while chunk c
   // is computed; every iteration issues the same loads (past the last
   // chunk the last record is read again), so the compiler's waits stay exact
-  ChunkOps<P, D> bufA, bufB;
-  if (nch > 0) load_ops<P, D>(bufA, rec_of(0), w, l, g, vt);
+  ChunkOps<D> bufA, bufB;
+  if (nch > 0) load_ops<D>(bufA, rec_of(0), w, l, g, vt);
   for (int c = 0; c < nch; c += 2) {
-    load_ops<P, D>(bufB, rec_of(c + 1), w, l, g, vt);
+    load_ops<D>(bufB, rec_of(c + 1), w, l, g, vt);
     step(bufA, c);
     if (c + 1 >= nch) break;
-    load_ops<P, D>(bufA, rec_of(c + 2), w, l, g, vt);
+    load_ops<D>(bufA, rec_of(c + 2), w, l, g, vt);
     step(bufB, c + 1);
   }
 
@@ -622,31 +574,32 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
   }
 }
 
-template <class P, int D>
+template <int D>
 static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
-  using In = typename P::In;
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   if (A.total_tokens > 0) {
-    hipLaunchKernelGGL((prefill_prep_kernel<P, D>), dim3((unsigned)slots, (unsigned)A.num_heads),
-                       dim3(kPrepThreads), 0, stream, (const In*)A.q, (const In*)A.k, (const In*)A.v,
-                       A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads,
-                       (unsigned char*)A.workspace, (int)A.scalar_gate, (int)A.raw_qkb);
-    const hipError_t e = hipGetLastError();
+    int* status = reinterpret_cast<int*>((unsigned char*)A.workspace + prefill_status_offset_f32(slots, A.num_heads, D));
+    hipError_t e = clear_prefill_status(status, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3((unsigned)slots, (unsigned)A.num_heads), dim3(kPrepThreads), 0,
+                       stream, (const float*)A.q, (const float*)A.k, (const float*)A.v, A.log_alpha,
+                       (const float*)A.beta, A.cu_seqlens, A.num_seqs, A.num_heads, (unsigned char*)A.workspace,
+                       (int)A.scalar_gate, (int)A.raw_qkb, status);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
   const int64_t groups = (pairs + 7) / 8;
   const unsigned blocks = (unsigned)(groups * 8 * (D / 16));
-  hipLaunchKernelGGL((prefill_state_kernel<P, D>), dim3(blocks), dim3(kThreads), 0, stream,
-                     A.cu_seqlens, A.num_seqs, A.num_heads, A.init_state, A.final_state,
-                     (In*)A.o, (const unsigned char*)A.workspace, A.state_indices, A.pool_slots);
+  hipLaunchKernelGGL((prefill_state_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
+                     A.num_heads, A.init_state, A.final_state, (float*)A.o, (const unsigned char*)A.workspace,
+                     A.state_indices, A.pool_slots);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs == 0) return hipSuccess;
-  return A.d == 128 ? launch_prefill_t<PathF32, 128>(A, stream)
-                    : launch_prefill_t<PathF32, 64>(A, stream);
+  return A.d == 128 ? launch_prefill_t<128>(A, stream) : launch_prefill_t<64>(A, stream);
 }
 
 }  // namespace kda

@@ -27,6 +27,9 @@
 // Kernel 2 (state pass) is one workgroup per (sequence, head, 16 value
 // columns): S's columns never mix in the recurrence.  Per chunk:
 //   E = U - W S;  O = Q' S + Bqk U;  S <- Diag(e^G[C-1]) S + Kc^T E.
+#include <algorithm>
+#include <cstddef>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_prefill_common.h"
@@ -43,6 +46,39 @@ using SplitB = Split<PathBF16>;
 constexpr int C = kChunk;
 constexpr size_t FB = 64 * sizeof(Frag);   // bytes per fragment
 constexpr int kPrepThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Record access.  A record is written by one workgroup and read by others
+// that may sit on another XCD, whose L2 is a different cache.  Every record
+// store and load therefore carries the SC1 cache-policy bit (device-scope
+// coherence, the policy of relaxed agent-scope atomics on gfx950): stores
+// reach the device coherence point before they are acknowledged and loads do
+// not return a stale copy from the local L1 or a non-coherent L2 line.  A
+// flag stored after the stores' acknowledgement then publishes the record
+// without a device-wide cache flush (an agent-scope fence writes back and
+// invalidates the whole L2, which costs more than the pass itself).
+// ---------------------------------------------------------------------------
+constexpr int kCoherent = 16;   // SC1
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc rec_rsrc(const unsigned char* rec, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rec), (short)0, (int)bytes, 0x00020000);
+}
+template <class T>
+__device__ __forceinline__ T ld_rec(Rsrc rs, size_t off) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "record loads are 8 or 16 bytes");
+  if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kCoherent));
+  else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, kCoherent));
+}
+template <class T>
+__device__ __forceinline__ void st_rec(Rsrc rs, size_t off, const T& x) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8 || sizeof(T) == 4, "record stores are 4, 8 or 16 bytes");
+  if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, (int)off, 0, kCoherent);
+  else if constexpr (sizeof(T) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), rs, (int)off, 0, kCoherent);
+  else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), rs, (int)off, 0, kCoherent);
+}
 
 // Per (chunk slot, head) record.
 template <int D>
@@ -113,26 +149,14 @@ __device__ __forceinline__ float row_shr(float v) {   // lane i of a DPP row get
 // k unnormalised and beta a logit (normalised in the kernel).  Both are
 // compile-time so that the input loads carry no branch.
 template <int D, bool SCALAR, bool RAW>
-__global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
+__device__ __forceinline__ void prep_item(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
-    const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
-    int N, int H, unsigned char* __restrict__ ws) {
+    const float* __restrict__ log_alpha, const In* __restrict__ beta, int H, int h, int64_t t0, int len,
+    unsigned char* __restrict__ rec, unsigned char* __restrict__ lds, int* __restrict__ status) {
   using R = Rec<D>;
   using L = PrepLds<D>;
   constexpr int KB = D / 32, NT = D / 16, SB = L::SB, PL = L::PL;
-  __shared__ __align__(16) unsigned char lds[L::BYTES];
-
-  // Slots in reverse order: the state pass starts from each sequence's first
-  // chunk, so those records, written last, are the ones most likely still
-  // held by the memory-side cache (records are stored with plain stores so
-  // that they are kept there).
-  const int64_t item = blockIdx.x;
-  const int64_t slot = (int64_t)(gridDim.x / H) - 1 - item / H;
-  const int h = (int)(item % H);
-  int n, len;
-  int64_t t0;
-  if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
-  unsigned char* rec = ws + ((size_t)slot * H + h) * R::BYTES;
+  const Rsrc rs = rec_rsrc(rec, R::BYTES);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, l16 = l & 15;
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     const float tc = tm + sTot[2 * D + key] + sTot[3 * D + key];
     if (tid < D) {
       sExpK[key] = __expf(tm);
-      *(reinterpret_cast<float*>(rec + R::G) + key) = __expf(tc);
+      st_rec<float>(rs, R::G + 4 * key, __expf(tc));
     } else if (tid < 2 * D) {
       sExpK[D + key] = __expf(tc - tm);
     }
@@ -266,6 +290,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   //   Kg = K e^G, Qg = Q e^G, Kc = K e^(G[C-1] - G)
   Frag kaF[KB], kbH[KB], kbL[KB], qaH[KB], qaL[KB];
   float qg[KB][8];
+  float dgmax = 0.f;   // largest |G - G[31]|: e^(+-80) is the most the factors may span
 #pragma unroll
   for (int p = 0; p < KB; ++p)
 #pragma unroll
@@ -278,6 +303,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
         const int m = 4 * hh + e;
         const float gm = gmv[p][hh][e];
         const float dg = gr[p][hh][e] - gm;
+        dgmax = fmaxf(dgmax, fabsf(dg));
         const float x = __expf(dg), ix = __expf(-dg);
         const float egm = egm4[e], ecm = ecm4[e];
         const float kx = (float)kr[p][hh][e] * rk, qx = (float)qr[p][hh][e] * rq;
@@ -299,12 +325,16 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     sKb(0, w, pb)[l] = kbH[pb];
     sKb(1, w, pb)[l] = kbL[pb];
   }
+  // a gate sum beyond the fp32 exponent range: report it (results of this
+  // chunk may be non-finite)
+  if (__any(dgmax > kMaxAnchoredExp) && l == 0)
+    __hip_atomic_fetch_or(status, kStatusGateRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 
   // ---- C: A = Ka Kbar^T (tiles (w, j)) and Bqk^T = Kbar Qa^T (tiles (j, w)),
   //      j <= w, in stages of SB key blocks; Kc^T fragments to the record ----
   for (int i = tid; i < NT * 2 * 64; i += kPrepThreads)
-    *(reinterpret_cast<HFrag*>(rec + R::KC) + i) = reinterpret_cast<const HFrag*>(lds + L::KCT)[i];
+    st_rec<HFrag>(rs, R::KC + 16 * (size_t)i, reinterpret_cast<const HFrag*>(lds + L::KCT)[i]);
   f32x4 accA[4], accB[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) accA[j] = accB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -467,7 +497,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
       wneg[it][e] = (In)(-wc[e]);
     }
     if (it & 1)
-      *(reinterpret_cast<HFrag*>(rec + R::W + ((w * KB + (it >> 1)) * 64 + l) * 16)) = wrec;
+      st_rec<HFrag>(rs, R::W + ((w * KB + (it >> 1)) * 64 + l) * 16, wrec);
   }
   __syncthreads();   // Kg^T and T are no longer read
 
@@ -487,7 +517,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf u16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) u16[e] = (_Float16)uc[e];
-    *(reinterpret_cast<HHalf*>(rec + R::U + ((ct * 4 + w) * 64 + l) * 8)) = u16;
+    st_rec<HHalf>(rs, R::U + ((ct * 4 + w) * 64 + l) * 8, u16);
     Half uh, ul;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -518,7 +548,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) qrec[4 * (it & 1) + e] = (_Float16)acc[e];
     if (it & 1)
-      *(reinterpret_cast<HFrag*>(rec + R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16)) = qrec;
+      st_rec<HFrag>(rs, R::QP + ((w * KB + (it >> 1)) * 64 + l) * 16, qrec);
   }
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
@@ -535,17 +565,36 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
     HHalf bu16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bu16[e] = (_Float16)bu[e];
-    *(reinterpret_cast<HHalf*>(rec + R::BU + ((ct * 4 + w) * 64 + l) * 8)) = bu16;
+    st_rec<HHalf>(rs, R::BU + ((ct * 4 + w) * 64 + l) * 8, bu16);
   }
 }
 
+// One (chunk slot, head) item of the two-kernel path: slots in reverse
+// order, so that the state pass, which starts from each sequence's first
+// chunk, finds those records -- written last -- in the memory-side cache.
+template <int D, bool SCALAR, bool RAW>
+__global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
+    int N, int H, unsigned char* __restrict__ ws, int* __restrict__ status) {
+  __shared__ __align__(16) unsigned char lds[PrepLds<D>::BYTES];
+  const int64_t item = blockIdx.x;
+  const int64_t slot = (int64_t)(gridDim.x / H) - 1 - item / H;
+  const int h = (int)(item % H);
+  int n, len;
+  int64_t t0;
+  if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
+  prep_item<D, SCALAR, RAW>(q, k, v, log_alpha, beta, H, h, t0, len, ws + ((size_t)slot * H + h) * Rec<D>::BYTES,
+                            lds, status);
+}
+
 // ---------------------------------------------------------------------------
-// Kernel 2: sequential pass over the chunks of one (sequence, head) for a
-// slice of VT value tiles (16 VT columns) of S.  Wave w owns key rows
-// [D/4 w, D/4 (w+1)) of the slice as accumulators and token tile w of every
-// chunk; the operands of the next two chunks are in flight while the
-// current one is computed.  W, Q' and Kc serve every value tile of the
-// slice, so a wider slice loads them once for more columns.
+// Sequential pass over the chunks of one (sequence, head) for a slice of VT
+// value tiles (16 VT columns) of S.  Wave w owns key rows [D/4 w, D/4 (w+1))
+// of the slice as accumulators and token tile w of every chunk; the operands
+// of the next two chunks are in flight while the current one is computed.
+// W, Q' and Kc serve every value tile of the slice, so a wider slice loads
+// them once for more columns.
 // ---------------------------------------------------------------------------
 template <int D, int VT>
 struct Ops {
@@ -560,62 +609,105 @@ struct Ops {
 // The operand loads of one chunk, in three parts that the step spreads over
 // its phases so that the vector memory path works while the MFMAs do.
 template <int D, int VT>
-__device__ __forceinline__ void load_ops_part(Ops<D, VT>& o, const unsigned char* __restrict__ rec, int part,
-                                              int w, int l, int g, int vt0) {
+__device__ __forceinline__ void load_ops_part(Ops<D, VT>& o, Rsrc rs, int part, int w, int l, int g, int vt0) {
   using R = Rec<D>;
   using O = Ops<D, VT>;
   if (part == 0) {
 #pragma unroll
-    for (int p = 0; p < O::KB; ++p)
-      o.w[p] = *reinterpret_cast<const HFrag*>(rec + R::W + ((w * O::KB + p) * 64 + l) * 16);
+    for (int p = 0; p < O::KB; ++p) o.w[p] = ld_rec<HFrag>(rs, R::W + ((w * O::KB + p) * 64 + l) * 16);
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-      o.u[t] = *reinterpret_cast<const HHalf*>(rec + R::U + (((vt0 + t) * 4 + w) * 64 + l) * 8);
-      o.bu[t] = *reinterpret_cast<const HHalf*>(rec + R::BU + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+      o.u[t] = ld_rec<HHalf>(rs, R::U + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+      o.bu[t] = ld_rec<HHalf>(rs, R::BU + (((vt0 + t) * 4 + w) * 64 + l) * 8);
     }
   } else if (part == 1) {
 #pragma unroll
-    for (int p = 0; p < O::KB; ++p)
-      o.qp[p] = *reinterpret_cast<const HFrag*>(rec + R::QP + ((w * O::KB + p) * 64 + l) * 16);
+    for (int p = 0; p < O::KB; ++p) o.qp[p] = ld_rec<HFrag>(rs, R::QP + ((w * O::KB + p) * 64 + l) * 16);
   } else {
 #pragma unroll
     for (int kt = 0; kt < O::KTW; ++kt)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int kti = w * O::KTW + kt;
-        o.kc[kt][p] = *reinterpret_cast<const HFrag*>(rec + R::KC + ((kti * 2 + p) * 64 + l) * 16);
+        o.kc[kt][p] = ld_rec<HFrag>(rs, R::KC + ((kti * 2 + p) * 64 + l) * 16);
       }
 #pragma unroll
     for (int kt = 0; kt < O::KTW; ++kt)
-      o.gam[kt] = *reinterpret_cast<const f32x4*>(rec + R::G + (16 * (w * O::KTW + kt) + 4 * g) * 4);
+      o.gam[kt] = ld_rec<f32x4>(rs, R::G + (16 * (w * O::KTW + kt) + 4 * g) * 4);
   }
 }
 
 template <int D, int VT>
-__device__ __forceinline__ void load_ops(Ops<D, VT>& o, const unsigned char* __restrict__ rec, int w, int l, int g,
-                                         int vt0) {
+__device__ __forceinline__ void load_ops(Ops<D, VT>& o, Rsrc rs, int w, int l, int g, int vt0) {
 #pragma unroll
-  for (int part = 0; part < 3; ++part) load_ops_part<D, VT>(o, rec, part, w, l, g, vt0);
+  for (int part = 0; part < 3; ++part) load_ops_part<D, VT>(o, rs, part, w, l, g, vt0);
 }
 
-// One workgroup per CU: the pass is bound by the operand bytes a CU keeps in
-// flight, and a second workgroup on the same CU lowers the throughput of
-// both (variable-length batches with more workgroups than CUs).
-template <int D, int VT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(
-    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin, In* __restrict__ o,
-    const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx, int pool_slots) {
-  using R = Rec<D>;
-  constexpr int NV = D / (16 * VT), KB = D / 32, KTW = D / 64;
+// Chunk-ready flags of the one-launch path: flag[slot * H + h] turns nonzero
+// once the record of (slot, h) is complete.  A wait gives up after about two
+// seconds (the whole prep of a million-token sequence takes milliseconds),
+// sets the status word and lets the pass run on with NaN outputs, so that no
+// wave can hang.
+constexpr int kSpinLimit = 1 << 21;
 
-  // XCD-aware order: the NV slices of one (sequence, head) share an XCD (and
-  // its L2) because workgroups are dealt to the 8 XCDs round-robin.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, rest = bid >> 3;
-  const int vt = rest % NV;
-  const int pair = (rest / NV) * 8 + xcd;
-  if (pair >= N * H) return;
-  const int n = pair / H, h = pair % H;
+struct Sync {
+  const int* flags;   // nullptr: records are complete before the pass starts
+  int* status;
+};
+
+// Readiness of the records a pass is about to load.  `upto` is the last
+// chunk known to be published; when chunk c is needed beyond it, lane i
+// polls chunk c + i % 16 (clamped to the last chunk) until chunk c is
+// published, and `upto` advances over the published run that starts at c.
+// A pass that trails the prep by more than 16 chunks thus polls once every
+// 16 steps, and one right behind it polls every step.  The acquire fence
+// keeps the record loads after the poll.
+__device__ __forceinline__ void need_record(const Sync& sy, int64_t slot0, int H, int h, int c, int nch, int lane,
+                                            int& upto, bool& failed) {
+  if (!sy.flags || failed || c <= upto) return;
+  const int* f = sy.flags + (slot0 + min(c + (lane & 15), nch - 1)) * H + h;
+  for (int spin = 0;; ++spin) {
+    const int ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t mask = __ballot(ready != 0) & 0xFFFFull;
+    if (mask & 1) {
+      upto = c + __builtin_ctzll(~mask) - 1;   // chunks c .. upto are published
+      break;
+    }
+    if (spin >= kSpinLimit) {
+      failed = true;
+      if (lane == 0) __hip_atomic_fetch_or(sy.status, kStatusWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// LDS of the state pass: S and E as B operands; S twice (by chunk parity)
+// when the read-out reads it again after the second barrier of a step.
+template <int D, int VT, bool HOLD_SF>
+struct StateLds {
+  static constexpr int KB = D / 32;
+  static constexpr size_t SB = (size_t)VT * KB * 64 * 16;        // one copy of S: HFrag [VT][KB][64]
+  static constexpr size_t S = 0;
+  static constexpr size_t E = S + (HOLD_SF ? 1 : 2) * SB;         // HFrag [VT][2][64]
+  static constexpr size_t BYTES = E + (size_t)VT * 2 * 64 * 16;
+};
+
+// The pass of (sequence n, head h, value slice vt).  NB operand buffers in
+// rotation (3: chunks c+1 and c+2 in flight during step c; 2: chunk c+1).
+// HOLD_SF keeps this step's S fragments in registers for both products;
+// otherwise the read-out reads them from LDS again, from a copy that the
+// next step does not overwrite.  Both give the same results bit for bit.
+template <int D, int VT, int NB, bool HOLD_SF>
+__device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H, const float* init, float* fin,
+                                           In* __restrict__ o, const unsigned char* __restrict__ ws,
+                                           const int32_t* __restrict__ sidx, int pool_slots, int n, int h, int vt,
+                                           const Sync& sy, unsigned char* __restrict__ lds) {
+  static_assert(NB == 2 || NB == 3, "two or three operand buffers");
+  using R = Rec<D>;
+  using SL = StateLds<D, VT, HOLD_SF>;
+  constexpr int KB = D / 32, KTW = D / 64;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
@@ -624,8 +716,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nch = (int)((eos - bos + kChunk - 1) / kChunk);
   const int64_t slot0 = bos / kChunk + n;
 
-  __shared__ HFrag sS[VT][KB][64];   // S as the B operand
-  __shared__ HFrag sE[VT][2][64];    // E as the B operand
+  HFrag (*sE)[2][64] = reinterpret_cast<HFrag (*)[2][64]>(lds + SL::E);   // E as the B operand
+  auto sS = [&](int c) {   // S as the B operand
+    return reinterpret_cast<HFrag (*)[KB][64]>(lds + SL::S + (HOLD_SF ? 0 : (c & 1) * SL::SB));
+  };
 
   const int64_t sslot = state_slot(sidx, pool_slots, n);
   if (sslot < 0) init = nullptr, fin = nullptr;
@@ -640,14 +734,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                       : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  auto rec_of = [&](int c) { return ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES; };
+  auto rec_of = [&](int c) {
+    return rec_rsrc(ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES, R::BYTES);
+  };
+  bool failed = false;   // a wait for records gave up: outputs and final state become NaN
+  int upto = -1;          // last chunk whose record is known to be published
 
   // one chunk step with operands `ops`; meanwhile the operands of a later
-  // chunk (record `nrec`) are loaded into `nxt`, one part per phase
-  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, const unsigned char* nrec) {
-    load_ops_part<D, VT>(nxt, nrec, 0, w, l, g, vt0);
+  // chunk (record `nrs`) are loaded into `nxt`, one part per phase
+  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, Rsrc nrs) {
+    need_record(sy, slot0, H, h, c + NB - 1, nch, l, upto, failed);
+    load_ops_part<D, VT>(nxt, nrs, 0, w, l, g, vt0);
     const int64_t t0 = bos + (int64_t)c * kChunk;
     const int len = (int)min<int64_t>(kChunk, eos - t0);
+    HFrag (*sSc)[KB][64] = sS(c);
 #pragma unroll
     for (int t = 0; t < VT; ++t)
 #pragma unroll
@@ -656,22 +756,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         HHalf hs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) hs[e] = (_Float16)S[t][kt][e];
-        *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sS[t][kti >> 1][l]) + 4 * (kti & 1)) = hs;
+        *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sSc[t][kti >> 1][l]) + 4 * (kti & 1)) = hs;
       }
     __syncthreads();
-    load_ops_part<D, VT>(nxt, nrec, 1, w, l, g, vt0);
+    load_ops_part<D, VT>(nxt, nrs, 1, w, l, g, vt0);
     // token tile w: W S first -- E gates the other waves; Q' S only after
     // the state update has been issued
-    HFrag sf[VT][KB];
+    HFrag sf[HOLD_SF ? VT : 1][KB];
+    if constexpr (HOLD_SF) {
 #pragma unroll
-    for (int t = 0; t < VT; ++t)
+      for (int t = 0; t < VT; ++t)
 #pragma unroll
-      for (int p = 0; p < KB; ++p) sf[t][p] = sS[t][p][l];
+        for (int p = 0; p < KB; ++p) sf[t][p] = sSc[t][p][l];
+    }
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       f32x4 wsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < KB; ++p) mma(wsum, ops.w[p], sf[t][p]);
+      for (int p = 0; p < KB; ++p) mma(wsum, ops.w[p], HOLD_SF ? sf[HOLD_SF ? t : 0][p] : sSc[t][p][l]);
       // E = U - W S, published as the B operand over tokens
       HHalf eh;
 #pragma unroll
@@ -679,7 +781,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[t][w >> 1][l]) + 4 * (w & 1)) = eh;
     }
     __syncthreads();
-    load_ops_part<D, VT>(nxt, nrec, 2, w, l, g, vt0);
+    load_ops_part<D, VT>(nxt, nrs, 2, w, l, g, vt0);
     // S <- Diag(e^G[C-1]) S + Kc^T E
 #pragma unroll
     for (int t = 0; t < VT; ++t)
@@ -696,37 +798,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[t][e];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], sf[t][p]);
+      for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], HOLD_SF ? sf[HOLD_SF ? t : 0][p] : sSc[t][p][l]);
       const int col = 16 * (vt0 + t) + l16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + 4 * g + e;
-        if (r < len) o[((t0 + r) * H + h) * D + col] = (In)qsum[e];
+        if (r < len) o[((t0 + r) * H + h) * D + col] = (In)(failed ? __builtin_nanf("") : qsum[e]);
       }
     }
   };
 
-  // three operand buffers in rotation: while chunk c is computed, chunk
-  // c+1's operands are in flight and chunk c+2's are being loaded (past the
-  // last chunk the last record is read again, so every step issues the same
-  // loads and the compiler's waits stay exact).  Twelve steps per loop
-  // iteration: at the loop head the compiler waits for most loads in flight,
-  // so the head is reached once every twelve chunks rather than every three.
+  // Operand buffers in rotation: while chunk c is computed, the operands of
+  // the next NB - 1 chunks are in flight (past the last chunk the last
+  // record is read again, so every step issues the same loads and the
+  // compiler's waits stay exact).  Twelve steps per loop iteration: at the
+  // loop head the compiler waits for most loads in flight, so the head is
+  // reached once every twelve chunks rather than every NB.  (The one-launch
+  // path checks that a record is published before the step that loads it.)
   Ops<D, VT> bufA, bufB, bufC;
   if (nch > 0) {
+    need_record(sy, slot0, H, h, 0, nch, l, upto, failed);
     load_ops<D, VT>(bufA, rec_of(0), w, l, g, vt0);
-    load_ops<D, VT>(bufB, rec_of(1), w, l, g, vt0);
+    if constexpr (NB == 3) {
+      need_record(sy, slot0, H, h, 1, nch, l, upto, failed);
+      load_ops<D, VT>(bufB, rec_of(1), w, l, g, vt0);
+    }
   }
   for (int c0 = 0; c0 < nch; c0 += 12) {
+    if constexpr (NB == 3) {
 #pragma unroll
-    for (int u = 0; u < 12; u += 3) {
-      const int c = c0 + u;
-      if (c >= nch) break;
-      step(bufA, c, bufC, rec_of(c + 2));
-      if (c + 1 >= nch) break;
-      step(bufB, c + 1, bufA, rec_of(c + 3));
-      if (c + 2 >= nch) break;
-      step(bufC, c + 2, bufB, rec_of(c + 4));
+      for (int u = 0; u < 12; u += 3) {
+        const int c = c0 + u;
+        if (c >= nch) break;
+        step(bufA, c, bufC, rec_of(c + 2));
+        if (c + 1 >= nch) break;
+        step(bufB, c + 1, bufA, rec_of(c + 3));
+        if (c + 2 >= nch) break;
+        step(bufC, c + 2, bufB, rec_of(c + 4));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 12; u += 2) {
+        const int c = c0 + u;
+        if (c >= nch) break;
+        step(bufA, c, bufB, rec_of(c + 1));
+        if (c + 1 >= nch) break;
+        step(bufB, c + 1, bufA, rec_of(c + 2));
+      }
     }
   }
 
@@ -736,36 +854,164 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int kt = 0; kt < KTW; ++kt) {
         const int kti = w * KTW + kt, col = 16 * (vt0 + t) + l16;
-        *reinterpret_cast<f32x4*>(fin + (sbase + col) * D + 16 * kti + 4 * g) = S[t][kt];
+        const float nanv = __builtin_nanf("");
+        *reinterpret_cast<f32x4*>(fin + (sbase + col) * D + 16 * kti + 4 * g) =
+            failed ? f32x4{nanv, nanv, nanv, nanv} : S[t][kt];
       }
   }
 }
 
+// Task index -> (sequence-head pair, value slice).  Tasks below nstatic (a
+// multiple of 8 NV) are dealt so that the NV slices of one (sequence, head)
+// share an XCD (and its L2), since workgroups are dealt to the 8 XCDs
+// round-robin and the first such block index is a multiple of 8; they cover
+// the pairs below nstatic / NV.  Later tasks go in pair order.
+template <int NV>
+__device__ __forceinline__ void task_of(int task, int nstatic, int& pair, int& vt) {
+  if (task < nstatic) {
+    const int xcd = task & 7, rest = task >> 3;
+    vt = rest % NV;
+    pair = (rest / NV) * 8 + xcd;
+  } else {
+    vt = task % NV;
+    pair = task / NV;
+  }
+}
+
+// Two-kernel path, kernel 2: one workgroup per (sequence, head, slice),
+// one workgroup per CU (the pass is bound by the operand bytes a CU keeps in
+// flight, and a second workgroup on the same CU lowers the throughput of
+// both when a batch has more workgroups than CUs).
+template <int D, int VT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_kernel(
+    const int32_t* __restrict__ cu, int N, int H, const float* init, float* fin, In* __restrict__ o,
+    const unsigned char* __restrict__ ws, const int32_t* __restrict__ sidx, int pool_slots) {
+  constexpr int NV = D / (16 * VT);
+  __shared__ __align__(16) unsigned char lds[StateLds<D, VT, true>::BYTES];
+  int pair, vt;
+  task_of<NV>(blockIdx.x, gridDim.x, pair, vt);
+  if (pair >= N * H) return;
+  state_task<D, VT, 3, true>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt, Sync{nullptr, nullptr},
+                             lds);
+}
+
+// ---------------------------------------------------------------------------
+// One-launch path: the prep and the state pass in one grid, so that the pass
+// follows the prep chunk by chunk instead of waiting for all of it, and the
+// CUs it leaves idle (a long sequence with few heads has few slices) run the
+// prep meanwhile.
+//   blocks [0, nstate):     state tasks, the first ones dealt statically,
+//                           then from a ticket;
+//   blocks [nstate, grid):  one prep item (chunk slot, head) each, in slot
+//                           order; its flag publishes its record.
+// Prep blocks wait for nothing, and the state blocks are at most a quarter
+// of the blocks the device holds at once, so prep blocks always find room
+// and every awaited record is eventually published, in whatever order the
+// blocks are dispatched.
+// Header words in the workspace: [0] state ticket, [1] status (bits
+// kStatus*); zeroed with the flags before each call.
+// ---------------------------------------------------------------------------
+struct FusedHdr {
+  int state_ticket, status, pad[62];
+};
+
+__global__ void fused_init_kernel(int* __restrict__ flags, int64_t nflags, FusedHdr* __restrict__ hdr) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = i; j < nflags; j += stride) flags[j] = 0;
+  if (i == 0) hdr->state_ticket = hdr->status = 0;
+}
+
+// The state role of the one-launch kernel shares the prep's register budget
+// (two blocks per CU): one-tile slices keep three operand buffers and hold
+// S's fragments; wider slices keep two and read S again from LDS.
+template <int VT>
+struct FusedState {
+  static constexpr int NB = VT == 1 ? 3 : 2;
+  static constexpr bool HOLD_SF = VT == 1;
+};
+
+__global__ void clear_status_kernel(int* status) {
+  if (threadIdx.x == 0) *status = 0;
+}
+
+template <int D, int VT>
+struct FusedLds {
+  using SL = StateLds<D, VT, FusedState<VT>::HOLD_SF>;
+  static constexpr size_t BYTES = PrepLds<D>::BYTES > SL::BYTES ? PrepLds<D>::BYTES : SL::BYTES;
+};
+
+template <int D, bool SCALAR, bool RAW, int VT>
+__global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
+    const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
+    const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
+    int N, int H, const float* init, float* fin, In* __restrict__ o, unsigned char* __restrict__ ws,
+    int* __restrict__ flags, FusedHdr* __restrict__ hdr, const int32_t* __restrict__ sidx, int pool_slots,
+    int nstate, int ntot) {
+  constexpr int NV = D / (16 * VT);
+  __shared__ __align__(16) unsigned char lds[FusedLds<D, VT>::BYTES];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= nstate) {
+    const int64_t item = (int64_t)blockIdx.x - nstate;
+    const int64_t slot = item / H;
+    const int h = (int)(item % H);
+    int n, len;
+    int64_t t0;
+    if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
+    prep_item<D, SCALAR, RAW>(q, k, v, log_alpha, beta, H, h, t0, len, ws + ((size_t)slot * H + h) * Rec<D>::BYTES,
+                              lds, &hdr->status);
+    // publish: every wave's record stores acknowledged, then the flag
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flags + slot * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  __shared__ int sTicket;
+  const Sync sy{flags, &hdr->status};
+  int task = blockIdx.x;
+  while (task < ntot) {
+    int pair, vt;
+    task_of<NV>(task, nstate, pair, vt);
+    if (pair < N * H)
+      state_task<D, VT, FusedState<VT>::NB, FusedState<VT>::HOLD_SF>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H,
+                                                                    pair % H, vt, sy, lds);
+    if (tid == 0) sTicket = nstate + atomicAdd(&hdr->state_ticket, 1);
+    __syncthreads();
+    task = sTicket;
+    __syncthreads();
+  }
+}
+
+// Workspace of the bf16 path: records, then one flag per (slot, head), then
+// the header.
+static size_t flags_offset(int64_t slots, int H, int d) {
+  const size_t rec = d == 128 ? Rec<128>::BYTES : Rec<64>::BYTES;
+  return (size_t)slots * H * rec;
+}
+static size_t hdr_offset(int64_t slots, int H, int d) {
+  return flags_offset(slots, H, d) + (((size_t)slots * H * sizeof(int) + 255) & ~(size_t)255);
+}
+
 template <int D>
-static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
+static hipError_t launch_two_kernel(const PrefillArgs& A, int vt, hipStream_t stream) {
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   const int64_t items = slots * A.num_heads;
   if (A.total_tokens > 0) {
+    FusedHdr* hdr = reinterpret_cast<FusedHdr*>((unsigned char*)A.workspace + hdr_offset(slots, A.num_heads, D));
+    hipLaunchKernelGGL(fused_init_kernel, dim3(1), dim3(64), 0, stream, (int*)nullptr, (int64_t)0, hdr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     auto kern = A.scalar_gate ? (A.raw_qkb ? prep_kernel<D, true, true> : prep_kernel<D, true, false>)
                               : (A.raw_qkb ? prep_kernel<D, false, true> : prep_kernel<D, false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                        (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens,
-                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace);
-    const hipError_t e = hipGetLastError();
+                       A.num_seqs, A.num_heads, (unsigned char*)A.workspace, &hdr->status);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // Slices of one value tile while they fit the CUs in one round: each
-  // chunk step is then shortest.  With more slices than CUs the pass is
-  // bound by throughput, and slices of two or four value tiles, which load
-  // W, Q' and Kc once for all their columns, do the same work with fewer
-  // operand bytes: the widest slice that still gives every CU a workgroup
-  // (the results are the same bit for bit).
   const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
   const int64_t groups = (pairs + 7) / 8;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  const int vt = pairs * (D / 64) >= cus ? 4 : pairs * (D / 32) >= cus ? 2 : 1;
   const unsigned blocks = (unsigned)(groups * 8 * (D / (16 * vt)));
   auto kern = vt == 4 ? state_kernel<D, 4> : vt == 2 ? state_kernel<D, 2> : state_kernel<D, 1>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs, A.num_heads,
@@ -774,9 +1020,99 @@ static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Scheduling overrides for measurements (0: automatic).
+#ifndef KDA_PREFILL_SCHEDULE
+#define KDA_PREFILL_SCHEDULE 0   // 1: two kernels, 2: one launch
+#endif
+#ifndef KDA_SLICE_TILES
+#define KDA_SLICE_TILES 0
+#endif
+
+// Returns false (and launches nothing) when the device cannot hold enough
+// blocks at once for the one-launch path.
+template <int D, int VT>
+static bool launch_fused_vt(const PrefillArgs& A, int cus, hipStream_t stream, hipError_t& err) {
+  constexpr int NV = D / (16 * VT);
+  auto kern = A.scalar_gate ? (A.raw_qkb ? fused_kernel<D, true, true, VT> : fused_kernel<D, true, false, VT>)
+                            : (A.raw_qkb ? fused_kernel<D, false, true, VT> : fused_kernel<D, false, false, VT>);
+  // state blocks: one per task, at most a quarter of the blocks the device
+  // holds at once, in whole groups of 8 NV
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kPrepThreads, 0) != hipSuccess) return false;
+  const int cap = ((per_cu * cus / 4) / (8 * NV)) * (8 * NV);
+  if (cap < 8 * NV) return false;
+  const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
+  const int ntasks = (int)(pairs * NV);
+  const int nstate = (int)std::min<int64_t>((((int64_t)ntasks + 8 * NV - 1) / (8 * NV)) * (8 * NV), cap);
+
+  const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
+  unsigned char* ws = (unsigned char*)A.workspace;
+  int* flags = reinterpret_cast<int*>(ws + flags_offset(slots, A.num_heads, D));
+  FusedHdr* hdr = reinterpret_cast<FusedHdr*>(ws + hdr_offset(slots, A.num_heads, D));
+  const int64_t items = slots * A.num_heads;
+  hipLaunchKernelGGL(fused_init_kernel, dim3((unsigned)std::min<int64_t>((items + 255) / 256, 1024)), dim3(256), 0,
+                     stream, flags, items, hdr);
+  err = hipGetLastError();
+  if (err != hipSuccess) return true;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nstate + items)), dim3(kPrepThreads), 0, stream, (const In*)A.q,
+                     (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs,
+                     A.num_heads, A.init_state, A.final_state, (In*)A.o, ws, flags, hdr, A.state_indices,
+                     A.pool_slots, nstate, std::max(nstate, ntasks));
+  err = hipGetLastError();
+  return true;
+}
+
+static int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  return cus;
+}
+
+
+template <int D>
+static hipError_t launch_t(const PrefillArgs& A, hipStream_t stream) {
+  const int cus = device_cus();
+  const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
+  if (A.total_tokens == 0 || KDA_PREFILL_SCHEDULE == 1) {
+    // Slices of one value tile while they fit the CUs in one round: each
+    // chunk step is then shortest.  With more slices than CUs the pass is
+    // bound by throughput, and slices of two or four value tiles, which load
+    // W, Q' and Kc once for all their columns, do the same work with fewer
+    // operand bytes: the widest slice that still gives every CU a workgroup
+    // (the results are the same bit for bit).
+    const int vt = pairs * (D / 64) >= cus ? 4 : pairs * (D / 32) >= cus ? 2 : 1;
+    return launch_two_kernel<D>(A, vt, stream);
+  }
+  // One launch: value slices of one tile while their tasks are at most a
+  // quarter of the blocks (each chunk step is shortest), else two, else four.
+  const int vt = KDA_SLICE_TILES ? KDA_SLICE_TILES
+                                 : (pairs * (D / 16) <= 2 * cus / 4 ? 1 : pairs * (D / 32) <= 2 * cus / 4 ? 2 : 4);
+  hipError_t err = hipSuccess;
+  const bool done = vt == 4 ? launch_fused_vt<D, 4>(A, cus, stream, err)
+                  : vt == 2 ? launch_fused_vt<D, 2>(A, cus, stream, err)
+                            : launch_fused_vt<D, 1>(A, cus, stream, err);
+  if (done) return err;
+  const int vt2 = pairs * (D / 64) >= cus ? 4 : pairs * (D / 32) >= cus ? 2 : 1;
+  return launch_two_kernel<D>(A, vt2, stream);
+}
+
 }  // namespace bf
 
 size_t prefill_record_bytes_bf16(int d) { return d == 128 ? bf::Rec<128>::BYTES : bf::Rec<64>::BYTES; }
+
+size_t prefill_workspace_bytes_bf16(int64_t slots, int num_heads, int d) {
+  return bf::hdr_offset(slots, num_heads, d) + sizeof(bf::FusedHdr);
+}
+
+size_t prefill_status_offset_bf16(int64_t slots, int num_heads, int d) {
+  return bf::hdr_offset(slots, num_heads, d) + offsetof(bf::FusedHdr, status);
+}
+
+hipError_t clear_prefill_status(int* status, hipStream_t stream) {
+  hipLaunchKernelGGL(bf::clear_status_kernel, dim3(1), dim3(64), 0, stream, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs == 0) return hipSuccess;

@@ -40,6 +40,16 @@ __device__ __forceinline__ int64_t state_slot(const int32_t* __restrict__ sidx, 
   return (s >= 0 && s < pool_slots) ? s : -1;
 }
 
+// Status word of a prefill call (in its workspace; see the C ABI's
+// kda_prefill_status_offset): zero when the call went as intended.
+constexpr int kStatusWaitGaveUp = 1;   // a wait for a chunk's factors gave up (NaN results)
+constexpr int kStatusGateRange = 2;    // a chunk's decay factors left the fp32 range
+// The decay factors are anchored at token 31 of the chunk: e^(G - G[31]) and
+// its inverse stay finite while |G - G[31]| <= 87 -- i.e. for log_alpha in
+// [-2.5, 0] and, more generally, while the gate sums over the 32 tokens on
+// either side of the anchor stay above -87.
+constexpr float kMaxAnchoredExp = 87.f;
+
 // four consecutive inputs of a token-major LDS row as fp32
 __device__ __forceinline__ f32x4 lds4(const __bf16* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);

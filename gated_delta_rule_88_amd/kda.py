@@ -44,6 +44,8 @@ def load(path: str = LIB_PATH):
     lib.kda_version.argtypes = []
     lib.kda_prefill_workspace_size.restype = sz
     lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    lib.kda_prefill_status_offset.restype = sz
+    lib.kda_prefill_status_offset.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
     lib.kda_prefill_varlen.restype = ctypes.c_int
     lib.kda_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
@@ -114,6 +116,23 @@ def workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv
                    dtype: torch.dtype) -> int:
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load().kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def status_offset(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                  dtype: torch.dtype) -> int:
+    """Byte offset of a prefill call's status word in its workspace."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_status_offset(num_seqs, total_tokens, num_heads, dk, dv, code))
+
+
+def prefill_status(workspace, num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                   dtype: torch.dtype) -> int:
+    """The status word a finished prefill call left in ``workspace`` (0: as
+    intended; bit 0: a wait for chunk factors gave up; bit 1: a chunk's decay
+    factors left the fp32 range).  Reads device memory, so it waits for the
+    call's stream."""
+    off = status_offset(num_seqs, total_tokens, num_heads, dk, dv, dtype)
+    return int(workspace[off:off + 4].view(torch.int32).item())
 
 
 def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
@@ -276,7 +295,9 @@ def kda_decode_step_pooled(q, k, v, log_alpha, beta, state_indices, state_pool, 
     _check(state_indices, "state_indices", (N,), torch.int32)
     _check(state_pool, "state_pool", (P, H, dv, dk), torch.float32)
     if o is None:
-        o = torch.empty((N, H, dv), device=q.device, dtype=dt)
+        # rows of sequences whose slot index is out of range are left
+        # untouched by the call: they come back as zeros
+        o = torch.zeros((N, H, dv), device=q.device, dtype=dt)
     _check(o, "o", (N, H, dv), dt)
     st = lib.kda_decode_step_pooled(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                     _ptr(state_indices), _ptr(state_pool), P, _ptr(o), N, H, dk, dv,

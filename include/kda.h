@@ -24,14 +24,19 @@
  *   nothing, copies nothing between host and device, never synchronises and
  *   keeps no global mutable state; it only enqueues kernels on `stream`
  *   (0 = the null stream), after reading the current device's compute-unit
- *   count, which picks the launch shape of the bf16 prefill's state pass
- *   (the results are the same bit for bit either way).  Buffers must stay
- *   valid until that work is done.
+ *   count and how many prefill workgroups a compute unit holds, which pick
+ *   the launch shape of the bf16 prefill (the results are the same bit for
+ *   bit either way).  Buffers must stay valid until that work is done.
  * - log_alpha is the natural logarithm of the decay gate alpha (fp32, <= 0):
  *   alpha_t[i] in (0, 1) decays key channel i (the per-channel gate of the
  *   "Kimi Linear Guide" page, section "2. Channel-Wise Data-Dependent
- *   Gating").  The GPU path supports log_alpha in [-2.5, 0]; values outside
- *   give undefined (possibly non-finite) results and are not checked.
+ *   Gating").  The decode step takes any finite log_alpha.  The prefill
+ *   forms each 64-token chunk's decay factors relative to its token 31, so
+ *   it needs the gate sums over the 32 tokens on either side of that token
+ *   to stay above -87 per channel (fp32 exponent range), which log_alpha in
+ *   [-2.5, 0] guarantees.  A chunk outside that range is not rejected: its
+ *   results may be non-finite and the call's status word reports it (see
+ *   kda_prefill_status_offset).
  * - beta is one scalar write strength per token and head (§03).
  * - q, k, v, beta and o share one element type `dtype`; the state is fp32.
  * - State layout (init_state, final_state, decode state):
@@ -44,8 +49,9 @@
  *   status; no exception or abort crosses this interface.  The contents of
  *   device arrays (cu_seqlens, gate values) are not inspected.
  * - Supported: dk == dv in {64, 128}; dtype KDA_BF16 or KDA_F32.
- * - Results are bitwise reproducible run to run on the same device (no
- *   atomics, fixed reduction order).
+ * - Results are bitwise reproducible run to run on the same device: every
+ *   sum has a fixed order; atomics only hand out work and publish
+ *   readiness, never accumulate values.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -84,12 +90,34 @@ int kda_version(void);
 /*
  * Bytes of device workspace kda_prefill_varlen needs for these sizes
  * (0 on invalid sizes).  Depends only on the arguments.  The workspace holds
- * per-chunk factors of the chunked form; its contents need not be
- * initialised and are meaningless after the call.
+ * per-chunk factors of the chunked form, and for bf16 one readiness flag
+ * per (chunk, head) and a small header; its contents need not be
+ * initialised on entry.  A workspace must not be shared by calls that may
+ * run at the same time.
  */
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t num_heads, int32_t dk, int32_t dv,
                                   kda_dtype dtype);
+
+/*
+ * Byte offset, inside the workspace of a prefill call with these sizes, of
+ * an int32 status word that the call sets (SIZE_MAX on invalid sizes).  It
+ * is meaningful once the call's work on the stream is done, for calls with
+ * total_tokens > 0; the caller reads it when it wants to (it is not
+ * returned, since the call does not wait for its kernels):
+ *   0   the call went as intended;
+ *   1   (bit 0) a wait of the bf16 path's state pass for a chunk's factors
+ *       gave up after about two seconds -- the device was shared so heavily
+ *       that the factors did not arrive; the affected sequences' outputs
+ *       and final states are NaN;
+ *   2   (bit 1) a chunk's decay factors left the fp32 range (gate sums
+ *       below -87 on one side of the chunk's anchor token); its results
+ *       may be non-finite.
+ * The pooled, Gated DeltaNet and raw-input prefill forms use the same word.
+ */
+size_t kda_prefill_status_offset(int32_t num_seqs, int64_t total_tokens,
+                                 int32_t num_heads, int32_t dk, int32_t dv,
+                                 kda_dtype dtype);
 
 /*
  * Chunk-parallel prefill over variable-length packed sequences

@@ -27,3 +27,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Parity margins of the session: max row and state error per checked
+    case against its tolerance."""
+    try:
+        from tests.parity import MARGINS
+    except Exception:  # pragma: no cover
+        return
+    if not MARGINS:
+        return
+    tr = terminalreporter
+    tr.section("parity margins (max relative error: output rows, final states; tolerance)")
+    for label, eo, es, tol in MARGINS:
+        worst = max(eo, es)
+        tr.write_line(f"{label:58s} o {eo:.2e}  state {es:.2e}  tol {tol:.0e}  "
+                      f"({worst / tol * 100:5.1f}% of tol)")

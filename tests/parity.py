@@ -17,6 +17,15 @@ import torch
 
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 
+# (label, output error, state error, tolerance) of every parity check in the
+# session, printed by the terminal summary hook in conftest.py so that the
+# margins appear at the end of the pytest output.
+MARGINS: list = []
+
+
+def record(label: str, err_o: float, err_s: float, tol: float) -> None:
+    MARGINS.append((label, float(err_o), float(err_s), float(tol)))
+
 
 def _np64(x):
     if isinstance(x, torch.Tensor):

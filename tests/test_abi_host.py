@@ -48,9 +48,12 @@ def test_status_strings_and_version(lib):
 
 def test_workspace_size(lib):
     f = lib.kda_prefill_workspace_size
-    # bf16 record: W, Q', Kc^T, U, Bqk U (fp16) + e^G (fp32)
+    # bf16: one record per (chunk slot, head) -- W, Q', Kc^T, U, Bqk U (fp16)
+    # and e^G (fp32) -- then one int32 chunk-ready flag per (slot, head)
+    # (padded to 256 bytes) and a 256-byte header
     rec_bf16_128 = 3 * 16384 + 2 * 16384 + 128 * 4
-    assert f(1, 8192, 32, 128, 128, BF16) == (8192 // 64 + 1 + 1) * 32 * rec_bf16_128
+    items = (8192 // 64 + 1 + 1) * 32
+    assert f(1, 8192, 32, 128, 128, BF16) == items * rec_bf16_128 + (items * 4 + 255) // 256 * 256 + 256
     assert f(1, 256, 1, 64, 64, F32) > 0
     assert f(0, 0, 1, 128, 128, BF16) > 0            # one spare slot per head
     assert f(1, 100, 2, 96, 96, BF16) == 0            # unsupported head size

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from gated_delta_rule_88_amd import inputs, kda
-from tests.parity import TOL, row_rel_err, state_rel_err
+from tests.parity import TOL, record, row_rel_err, state_rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,6 +50,7 @@ def check(d, tol, label):
     ro, rf = run_oracle(d)
     eo, es = row_rel_err(o, ro), state_rel_err(f, rf)
     _log(f"{label}: max row-rel err o {eo:.3e}, state {es:.3e} (tol {tol:g})")
+    record(label, eo, es, tol)
     assert eo <= tol and es <= tol, (label, eo, es)
     return o, f
 
@@ -83,11 +84,13 @@ def test_many_short_sequences(dtype, D):
     check(d, TOL[dtype], f"257 short sequences {dtype} D={D}")
 
 
-@pytest.mark.parametrize("nseq,H", [(7, 3), (20, 4), (75, 4)], ids=["1-tile", "2-tile", "4-tile"])
+@pytest.mark.parametrize("nseq,H", [(5, 3), (8, 4), (75, 4)], ids=["1-tile", "2-tile", "4-tile"])
 def test_state_pass_slice_widths(nseq, H):
-    """the bf16 state pass takes slices of 1, 2 or 4 value tiles depending on
-    how many (sequence, head) pairs there are against the CUs (21, 80 and 300
-    pairs here, on a 256-CU device); every width must match the oracle"""
+    """the bf16 state pass takes slices of 1, 2 or 4 value tiles: the
+    narrowest whose tasks are at most a quarter of the blocks the device
+    holds at once (15, 32 and 300 (sequence, head) pairs here, on a 256-CU
+    device: 120, 128 and 600 tasks -- the last dealt partly from the state
+    ticket); every width must match the oracle"""
     lengths = np.random.default_rng(490 + nseq).integers(1, 200, size=nseq).tolist()
     d = make_case(lengths, H=H, D=128, dtype=torch.bfloat16, seed=491 + nseq)
     check(d, TOL[torch.bfloat16], f"state pass slice width, {nseq} x {H} pairs")
@@ -116,6 +119,63 @@ def test_strong_decay_edge_of_domain():
     d = make_case([192, 77], H=2, D=128, dtype=torch.float32, seed=9, u_range=(0.85, 0.916))
     assert float(d["log_alpha"].min()) >= -2.5
     check(d, TOL[torch.float32], "strong decay f32")
+
+
+@pytest.mark.parametrize("gate", ["kda", "gdn"])
+def test_bf16_strong_decay_edge_of_domain(gate):
+    """bf16 path at the bottom of the gate range, log_alpha in (-2.5, -2.34)
+    everywhere: the anchored decay factors then span e^(+-78), which only the
+    bf16 operands of the prep carry (channel gates and, for Gated DeltaNet,
+    one gate per token and head)"""
+    d = make_case([192, 77, 130], H=2, D=128, dtype=torch.bfloat16, seed=19, u_range=(0.85, 0.916))
+    if gate == "gdn":
+        d["log_alpha"] = d["log_alpha"][..., 0].contiguous()
+    assert float(d["log_alpha"].min()) >= -2.5
+    g = to_dev(d)
+    fn = kda.gdn_prefill_varlen if gate == "gdn" else kda.kda_prefill_varlen
+    o, f = fn(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["cu_seqlens"], g["init_state"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill_scalar_gate if gate == "gdn" else oracle.prefill
+    ro, rf = ref(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"].long(), d["init_state"])
+    eo, es = row_rel_err(o, ro), state_rel_err(f, rf)
+    _log(f"strong decay bf16 {gate}: o {eo:.3e} state {es:.3e}")
+    record(f"strong decay bf16 {gate}", eo, es, TOL[torch.bfloat16])
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_status_word_reports_gate_range(dtype):
+    """a call inside the gate range leaves the status word 0; a run of
+    log_alpha = -6 (gate sums far below -87 across a chunk's anchor) sets its
+    gate-range bit and nothing else"""
+    lengths = [150, 90]
+    d = make_case(lengths, H=2, D=128, dtype=dtype, seed=23)
+    T, H, D = d["q"].shape
+    g = to_dev(d)
+    ws = torch.empty(kda.workspace_size(2, T, H, D, D, dtype), device=DEV, dtype=torch.uint8)
+    kda.kda_prefill_varlen(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["cu_seqlens"],
+                           g["init_state"], workspace=ws)
+    assert kda.prefill_status(ws, 2, T, H, D, D, dtype) == 0
+    la = g["log_alpha"].clone()
+    la[10:60] = -6.0   # the first chunk of sequence 0 around its token 31
+    kda.kda_prefill_varlen(g["q"], g["k"], g["v"], la, g["beta"], g["cu_seqlens"], g["init_state"],
+                           workspace=ws)
+    assert kda.prefill_status(ws, 2, T, H, D, D, dtype) == 2
+    # and the next in-range call clears it
+    kda.kda_prefill_varlen(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["cu_seqlens"],
+                           g["init_state"], workspace=ws)
+    assert kda.prefill_status(ws, 2, T, H, D, D, dtype) == 0
+
+
+@pytest.mark.parametrize("scale", [2000.0, 7000.0])
+def test_bf16_large_values(scale):
+    """bf16 path with values scaled up: the sequential pass multiplies fp16
+    operands (U, E, S and the read-out terms), so the results hold while
+    those stay below the fp16 range (6.5e4); |v| up to 4.3 * scale here"""
+    d = make_case([150, 90], H=2, D=128, dtype=torch.bfloat16, seed=25)
+    d["v"] = (d["v"].float() * scale).to(torch.bfloat16)
+    d["init_state"] = d["init_state"] * scale
+    check(d, TOL[torch.bfloat16], f"bf16 values x{scale:g}")
 
 
 def test_no_write_identity_is_bitwise():

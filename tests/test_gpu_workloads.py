@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from gated_delta_rule_88_amd import inputs, kda
-from tests.parity import TOL, row_rel_err, state_rel_err
+from tests.parity import TOL, record, row_rel_err, state_rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -47,6 +47,7 @@ def test_prefill_8k_full():
     ro, rf = _oracle_cols(d, slice(None))
     eo, es = row_rel_err(o, ro), state_rel_err(f, rf)
     _log(f"prefill_8k: o {eo:.3e} state {es:.3e}")
+    record("prefill_8k (all outputs and states)", eo, es, BF16_TOL)
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
@@ -59,6 +60,7 @@ def test_varlen_16_full():
     ro, rf = _oracle_cols(d, cols)
     eo, es = row_rel_err(o[..., cols], ro), state_rel_err(f[:, :, cols, :], rf)
     _log(f"varlen_16 cols 48..63: o {eo:.3e} state {es:.3e}")
+    record("varlen_16 (cols 48..63)", eo, es, BF16_TOL)
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
@@ -76,6 +78,7 @@ def test_long_1m_drift():
     ro, rf = _oracle_cols(d, cols, out_rows=rows)
     eo, es = row_rel_err(osel, ro), state_rel_err(fsel, rf)
     _log(f"long_1m cols 112..127, {len(rows)} rows: o {eo:.3e} state {es:.3e}")
+    record("long_1m (cols 112..127, strided rows)", eo, es, BF16_TOL)
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
@@ -104,4 +107,5 @@ def test_decode_256_all_steps():
     es = state_rel_err(state[:, :, cols, :], ref)
     _log(f"decode_256 cols 0..15, {steps} steps: o {worst:.3e} state {es:.3e} "
          f"(oracle {time.time() - t:.1f}s)")
+    record("decode_256 (cols 0..15, 512 steps)", worst, es, BF16_TOL)
     assert worst <= BF16_TOL and es <= BF16_TOL
