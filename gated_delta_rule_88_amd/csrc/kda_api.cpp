@@ -5,6 +5,10 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
+#include <hip/hip_runtime.h>
+
 #include "kda_launch.h"
 
 namespace {
@@ -19,6 +23,22 @@ kda_status check_common(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t
   return KDA_OK;
 }
 
+// Checks of a prefill call's arguments other than the workspace.
+kda_status prefill_check(const void* q, const void* k, const void* v, const float* log_alpha, const void* beta,
+                         const int32_t* cu_seqlens, const float* init_state, void* o, float* final_state,
+                         int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                         kda_dtype dtype) {
+  kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
 kda_status prefill_plain(const void* q, const void* k, const void* v,
                               const float* log_alpha, const void* beta,
                               const int32_t* cu_seqlens, const float* init_state,
@@ -26,14 +46,10 @@ kda_status prefill_plain(const void* q, const void* k, const void* v,
                               int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                               kda_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, bool scalar_gate, bool raw) {
-  kda_status st = check_common(num_seqs, num_heads, dk, dv, dtype);
+  kda_status st = prefill_check(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
+                                total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_OK) return st;
-  if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX) return KDA_ERR_SHAPE;
-  if (!cu_seqlens) return KDA_ERR_NULL;
-  if (total_tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  if (workspace && !aligned16(workspace)) return KDA_ERR_ALIGN;
   const size_t need = kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype);
   if (total_tokens > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
 
@@ -82,6 +98,7 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_DTYPE: return "unknown element type";
     case KDA_ERR_HIP: return "kernel launch failed";
+    case KDA_ERR_SCRATCH: return "sizes exceed the no-allocation prefill's scratch array";
   }
   return "unknown status";
 }
@@ -254,3 +271,50 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Prefill without allocation.  Its workspace is a device array of this
+// library: each GPU that runs the library holds its own copy (at its own
+// address) until the process ends.  In host code the array's name is only a
+// host-side stand-in, so the device address is looked up with
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed on (to the kernels, as the workspace).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];   // per device; set once, never changed
+
+kda_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return KDA_OK;
+}
+}  // namespace
+
+kda_status kda_prefill_varlen_noalloc(const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const void* beta,
+                                      const int32_t* cu_seqlens, const float* init_state,
+                                      void* o, float* final_state, int32_t num_seqs,
+                                      int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                      kda_dtype dtype, hipStream_t stream) {
+  kda_status st = prefill_check(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
+                                total_tokens, num_heads, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  void* ws = nullptr;
+  if (total_tokens > 0) {
+    if (kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) > KDA_NOALLOC_SCRATCH_BYTES)
+      return KDA_ERR_SCRATCH;
+    st = scratch_address(&ws);
+    if (st != KDA_OK) return st;
+  }
+  return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs, total_tokens,
+                       num_heads, dk, dv, dtype, ws, KDA_NOALLOC_SCRATCH_BYTES, stream, false, false);
+}

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "_build", "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
-           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_DTYPE", 7: "KDA_ERR_HIP"}
+           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_DTYPE", 7: "KDA_ERR_HIP",
+           8: "KDA_ERR_SCRATCH"}
 
 _lib = None
 
@@ -49,6 +50,9 @@ def load(path: str = LIB_PATH):
     lib.kda_prefill_varlen.restype = ctypes.c_int
     lib.kda_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        i32, i64, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kda_prefill_varlen_noalloc.restype = ctypes.c_int
+    lib.kda_prefill_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i32, i64, i32, i32, i32, ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
@@ -135,6 +139,15 @@ def prefill_status(workspace, num_seqs: int, total_tokens: int, num_heads: int, 
     return int(workspace[off:off + 4].view(torch.int32).item())
 
 
+def kda_prefill_varlen_noalloc(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
+                               o=None, final_state=None, want_final: bool = True):
+    """:func:`kda_prefill_varlen` through the entry point that allocates
+    nothing: its workspace is the library's own scratch array (one per GPU).
+    Outputs the caller does not pass are allocated here, before the call."""
+    return _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, o=o, final_state=final_state,
+                    want_final=want_final, workspace=None, scalar_gate=False, noalloc=True)
+
+
 def kda_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
                        o=None, final_state=None, want_final: bool = True, workspace=None):
     return _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, o=o, final_state=final_state,
@@ -158,7 +171,7 @@ def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, *,
 
 
 def _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, *, o, final_state, want_final,
-             workspace, scalar_gate, raw=False):
+             workspace, scalar_gate, raw=False, noalloc=False):
     """Chunked prefill over packed sequences; returns ``(o, final_state)``.
 
     q, k ``[T,H,dk]``; v ``[T,H,dv]`` (bf16 or fp32, one dtype); log_alpha
@@ -187,6 +200,13 @@ def _prefill(q, k, v, log_alpha, beta, cu_seqlens, init_state, *, o, final_state
         final_state = torch.empty((N, H, dv, dk), device=q.device, dtype=torch.float32)
     if final_state is not None:
         _check(final_state, "final_state", (N, H, dv, dk), torch.float32)
+    if noalloc:
+        st = lib.kda_prefill_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                            _ptr(cu_seqlens), _ptr(init_state), _ptr(o), _ptr(final_state),
+                                            N, T, H, dk, dv, code, _stream(q.device))
+        if st != 0:
+            raise KdaError(st, "kda_prefill_varlen_noalloc")
+        return o, final_state
     need = int(lib.kda_prefill_workspace_size(N, T, H, dk, dv, code))
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)

@@ -22,7 +22,9 @@
  * - All tensor arguments are DEVICE pointers to contiguous, row-major
  *   buffers, 16-byte aligned, owned by the caller.  The library allocates
  *   nothing, copies nothing between host and device, never synchronises and
- *   keeps no global mutable state; it only enqueues kernels on `stream`
+ *   keeps no global mutable state (kda_prefill_varlen_noalloc aside: it
+ *   looks up, once per device, the address of the library's scratch array);
+ *   it only enqueues kernels on `stream`
  *   (0 = the null stream), after reading the current device's compute-unit
  *   count and how many prefill workgroups a compute unit holds, which pick
  *   the launch shape of the bf16 prefill (the results are the same bit for
@@ -73,7 +75,8 @@ typedef enum kda_status {
   KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   KDA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
   KDA_ERR_DTYPE = 6,       /* unknown element type */
-  KDA_ERR_HIP = 7          /* a kernel launch failed */
+  KDA_ERR_HIP = 7,         /* a kernel launch failed */
+  KDA_ERR_SCRATCH = 8      /* sizes exceed kda_prefill_varlen_noalloc's scratch array */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -328,6 +331,37 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
                                 kda_dtype dtype,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * kda_prefill_varlen without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The call itself allocates nothing (no
+ * hipMalloc, no allocating library routine); its workspace is a device array
+ * of KDA_NOALLOC_SCRATCH_BYTES bytes built into the library, of which each
+ * GPU that runs the library holds one copy from the first load of the
+ * library's kernels until the process ends.  Arguments, layouts and results
+ * are exactly those of kda_prefill_varlen (same kernels).
+ *
+ * Limits and sharing: sizes whose kda_prefill_workspace_size(...) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_SCRATCH before any HIP call (for
+ * bf16 and dk = 128 that is about 4,880 (64-token chunk, head) pairs, e.g.
+ * 8K tokens of 32 heads in one sequence).  Every call on a GPU uses that
+ * GPU's one array, so calls that may run at the same time on one GPU (on
+ * different streams, or from different threads) race and must not be
+ * issued; calls in one stream are ordered and safe.  Each call clears what
+ * must start at zero itself.  The status word of kda_prefill_status_offset
+ * lives in the array and is not exposed for these calls.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)384 << 20)
+
+kda_status kda_prefill_varlen_noalloc(const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const void* beta,
+                                      const int32_t* cu_seqlens,
+                                      const float* init_state,
+                                      void* o, float* final_state,
+                                      int32_t num_seqs, int64_t total_tokens,
+                                      int32_t num_heads, int32_t dk, int32_t dv,
+                                      kda_dtype dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

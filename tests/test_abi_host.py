@@ -190,3 +190,18 @@ def backward(lib, **over):
 ])
 def test_backward_rejects(lib, over, expect):
     assert backward(lib, **over) == expect
+
+
+def test_noalloc_prefill_rejects_before_any_hip_call(lib):
+    """kda_prefill_varlen_noalloc: argument checks, and sizes whose workspace
+    exceeds the library's scratch array, return before any HIP call"""
+    f = lib.kda_prefill_varlen_noalloc
+    p = ctypes.c_void_p(0x10000)   # aligned, never dereferenced
+    T, H = 16384, 32
+    big = lib.kda_prefill_workspace_size(1, T, H, 128, 128, BF16)
+    assert big > (384 << 20)
+    assert f(p, p, p, p, p, p, None, p, None, 1, T, H, 128, 128, BF16, None) == 8   # KDA_ERR_SCRATCH
+    assert f(p, p, p, p, p, None, None, p, None, 1, T, H, 128, 128, BF16, None) == NULL
+    assert f(p, p, p, p, p, ctypes.c_void_p(0x10004), None, p, None, 1, T, H, 128, 128, BF16, None) == ALIGN
+    assert f(p, p, p, p, p, p, None, p, None, 1, T, H, 96, 96, BF16, None) == UNSUP
+    assert kda.status_string(8) == "sizes exceed the no-allocation prefill's scratch array"
