@@ -18,7 +18,13 @@ Prints one JSON line:
                H = 16) prefill workloads: tokens/s and HBM fraction per call
   backward     kda_prefill_backward on the 8K workload (gradients of every
                input for seeded upstream gradients), against the fp32 MFMA peak
-  cpu_baseline the fp64 oracle on the host cores, same prefill workload
+  cpu_baseline the fp64 oracle on the host cores: the 8K prefill workload
+               (headline), plus per_workload rates of the variable-length,
+               long-context and decode workloads (the last two on the value
+               columns the parity tests check), with the host's CPU model,
+               nproc and usable cores
+  ceilings     a measured 1 GiB device-to-device copy, beside the 8 TB/s spec;
+               every HBM fraction is also given against it (frac_of_copy)
 
 Other modes:
   --part prefill|decode|backward|copy
@@ -102,24 +108,132 @@ def decode_algorithmic(N, H, d):
     return N * H * (2 * d * d * 4 + 4 * d * 2 + d * 4 + 2)
 
 
-def cpu_baseline(prefill_inputs):
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cores": usable}
+
+
+def _host(X, cols=None):
+    h = {k: X[k].cpu() for k in ("q", "k", "log_alpha", "beta")}
+    h["v"] = X["v"].cpu() if cols is None else X["v"][..., cols].cpu().contiguous()
+    init = X.get("init_state")
+    h["init_state"] = None if init is None else (init.cpu() if cols is None else init[:, :, cols, :].cpu())
+    h["cu"] = X["cu_seqlens"].cpu().long()
+    return h
+
+
+def _oracle_prefill(h, threads, out_rows=None):
     import oracle
-    d = prefill_inputs
-    host = {k: d[k].cpu() for k in ("q", "k", "v", "log_alpha", "beta")}
-    cu = d["cu_seqlens"].cpu().long()
+    oracle.prefill(h["q"], h["k"], h["v"], h["log_alpha"], h["beta"], h["cu"], h["init_state"],
+                   nthreads=threads, want_final=True, out_rows=out_rows)
+
+
+def cpu_baseline(prefill_inputs, dev):
+    """The fp64 oracle on the host cores: the 8K prefill workload repeated
+    for about 5 s (the headline figure), then one pass over each of the other
+    workloads -- the variable-length batch whole, the long-context sequence
+    and the decode sequence on the 16 value columns their parity tests check
+    (columns never mix, so a column slice is exactly 1/8 of the work; the
+    whole-workload rate is the slice's divided by 8)."""
+    import oracle
+    import torch
+    from gated_delta_rule_88_amd import inputs
     threads = oracle.default_threads()
-    T = host["q"].shape[0]
-    # repeat the whole call until about 10 s of host time have passed
+    h = _host(prefill_inputs)
+    T, H, D = h["q"].shape
     reps, t0 = 0, time.perf_counter()
-    while reps < 100 and (reps == 0 or time.perf_counter() - t0 < 10.0):
-        oracle.prefill(host["q"], host["k"], host["v"], host["log_alpha"], host["beta"], cu, None,
-                       nthreads=threads, want_final=True)
+    while reps < 100 and (reps == 0 or time.perf_counter() - t0 < 5.0):
+        _oracle_prefill(h, threads)
         reps += 1
     dt = (time.perf_counter() - t0) / reps
-    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole 8K prefill workload (T={T}, H={host['q'].shape[1]}, "
-                      f"d={host['q'].shape[2]}, final state), fp64 token recurrence, "
-                      f"{reps} calls, {dt:.3f} s each"}
+    per = {"prefill_8k": {"tokens_per_s": round(T / dt, 1), "s": round(dt, 3), "calls": reps,
+                          "sample": "whole workload"}}
+
+    X = inputs.prefill_inputs(inputs.WORKLOADS["varlen_16"], device=dev)
+    hv = _host(X)
+    del X
+    t0 = time.perf_counter()
+    _oracle_prefill(hv, threads)
+    dt = time.perf_counter() - t0
+    Tv = hv["q"].shape[0]
+    per["varlen_16"] = {"tokens_per_s": round(Tv / dt, 1), "s": round(dt, 3), "tokens": Tv,
+                        "sample": "whole workload (16 sequences, initial and final states)"}
+    del hv
+
+    wl = inputs.WORKLOADS["long_1m"]
+    X = inputs.prefill_inputs(wl, device=dev)
+    hl = _host(X, cols=slice(112, 128))
+    del X
+    torch.cuda.empty_cache()
+    Tl = hl["q"].shape[0]
+    import numpy as np
+    rows = np.unique(np.concatenate([np.arange(0, Tl, 4096), [Tl - 1]]))
+    t0 = time.perf_counter()
+    _oracle_prefill(hl, threads, out_rows=rows)
+    dt = time.perf_counter() - t0
+    per["long_1m"] = {"tokens_per_s_columns_112_127": round(Tl / dt, 1),
+                      "tokens_per_s": round(Tl / dt / 8, 1), "s": round(dt, 3),
+                      "sample": "all 2^20 tokens, value columns 112..127 (1/8 of the work), outputs kept on "
+                                "the strided rows t = 0 mod 4096 and T-1; tokens_per_s = column rate / 8"}
+    del hl
+
+    dwl = inputs.WORKLOADS["decode_256"]
+    Dd = inputs.decode_inputs(dwl, device=dev, steps=64)
+    cols = slice(0, 16)
+    hd = {k: Dd[k].cpu() for k in ("q", "k", "log_alpha", "beta")}
+    hd["v"] = Dd["v"][..., cols].cpu().contiguous()
+    ref = Dd["state"][:, :, cols, :].cpu().double().numpy()
+    del Dd
+    steps = 512
+    t0 = time.perf_counter()
+    for s in range(steps):
+        j = s % 64
+        _, ref = oracle.decode_step(hd["q"][j], hd["k"][j], hd["v"][j], hd["log_alpha"][j], hd["beta"][j], ref,
+                                    nthreads=threads)
+    dt = time.perf_counter() - t0
+    ntok = dwl.num_seqs * steps
+    per["decode_256"] = {"tokens_per_s_columns_0_15": round(ntok / dt, 1), "tokens_per_s": round(ntok / dt / 8, 1),
+                         "s": round(dt, 3),
+                         "sample": "512 consecutive steps of 256 sequences x 32 heads (inputs cycling over 64 "
+                                   "resident steps, as on the GPU), value columns 0..15 (1/8 of the work); "
+                                   "tokens_per_s = column rate / 8"}
+    return {"value": per["prefill_8k"]["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole 8K prefill workload (T={T}, H={H}, d={D}, final state), fp64 token "
+                      f"recurrence, {per['prefill_8k']['calls']} calls, {per['prefill_8k']['s']:.3f} s each",
+            "host": host_info(), "per_workload": per}
+
+
+def copy_ceiling(dev, K=10):
+    """GB/s of a plain 1 GiB device-to-device copy (read + write bytes)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ms = []
+    for _ in range(K):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * COPY_BYTES / (ms[K // 2] * 1e-3) / 1e9, 1)
 
 
 def stored_traffic():
@@ -140,7 +254,7 @@ def stored_traffic():
 # ---------------------------------------------------------------------------
 # kernels read from each part's run
 PART_KERNELS = {"copy": {"copy": "copyBuffer"},
-                "prefill": {"prep": "prep_kernel", "state": "state_kernel"},
+                "prefill": {"prefill": "fused_kernel", "init": "fused_init_kernel"},
                 "decode": {"decode": "decode_step_kernel"}}
 
 
@@ -184,16 +298,13 @@ def run_traffic(outdir):
         c = rec[k]
         return (c["FETCH_SIZE"] * rec["copy_factor_fetch"] + c["WRITE_SIZE"] * rec["copy_factor_write"]) * 1024
 
-    rec["prefill_call_bytes"] = scaled("prep") + scaled("state")
-    rec["prep_bytes"] = scaled("prep")
-    rec["state_bytes"] = scaled("state")
+    rec["prefill_call_bytes"] = scaled("prefill") + scaled("init")
     rec["decode_call_bytes"] = scaled("decode")
     for path in (os.path.join(outdir, "traffic_record.json"), TRAFFIC_RECORD):
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as fh:
             json.dump(rec, fh, indent=1)
-    print(json.dumps({k: rec[k] for k in ("prefill_call_bytes", "prep_bytes", "state_bytes",
-                                          "decode_call_bytes", "copy_factor_fetch",
+    print(json.dumps({k: rec[k] for k in ("prefill_call_bytes", "decode_call_bytes", "copy_factor_fetch",
                                           "copy_factor_write")}), flush=True)
 
 
@@ -422,6 +533,7 @@ def main():
     pre_avg = sum(pre_ms) / K
     dec_avg = sum(dec_ms) / K
 
+    copy_gbps = copy_ceiling(dev)
     pbytes, pflops = prefill_algorithmic(T, H, D, 1, False, True)
     dbytes = decode_algorithmic(dwl.num_seqs, dwl.heads, dwl.dv)
     pre_gbps = pbytes / (pre_avg * 1e-3) / 1e9
@@ -430,13 +542,16 @@ def main():
     roof_pre = {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": round(traffic["prefill_call_bytes"]) if traffic else None,
+                "frac_of_copy": round(pre_gbps / copy_gbps, 4),
                 "algorithmic_bytes": pbytes,
-                "launch": "kda_prefill_varlen: prep_kernel then state_kernel (one call)",
+                "launch": "kda_prefill_varlen: fused_init_kernel, then fused_kernel (prep blocks and "
+                          "state-pass blocks in one grid)",
                 "mfma_tflops": round(pflops / (pre_avg * 1e-3) / 1e12, 2),
                 "mfma_frac": round(pflops / (pre_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": round(traffic["decode_call_bytes"]) if traffic else None,
+                "frac_of_copy": round(dec_gbps / copy_gbps, 4),
                 "algorithmic_bytes": dbytes,
                 "launch": "kda_decode_step: decode_step_kernel"}
     dominant = roof_dec if dec_avg > pre_avg else roof_pre
@@ -468,6 +583,7 @@ def main():
                    "sequence_512": {"ms_per_step": round(min(seq_ms), 5),
                                     "GB_s": round(dbytes / (min(seq_ms) * 1e-3) / 1e9, 1),
                                     "frac_hbm": round(dbytes / (min(seq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                    "frac_of_copy": round(dbytes / (min(seq_ms) * 1e-3) / 1e9 / copy_gbps, 4),
                                     "repeats": 3},
                    "value": round(dec_gbps, 1), "unit": "GB/s",
                    "tokens_per_s": round(dwl.num_seqs / (dec_avg * 1e-3), 1), "roofline": roof_dec},
@@ -476,7 +592,7 @@ def main():
                         "GB_s": round(gdn_prefill_algorithmic(T, H, D, 1, True) / (sum(gdn_ms) / K * 1e-3) / 1e9, 1),
                         "frac_hbm": round(gdn_prefill_algorithmic(T, H, D, 1, True) / (sum(gdn_ms) / K * 1e-3)
                                           / 1e9 / HBM_PEAK_GBPS, 4),
-                        "launch": "kda_gdn_prefill_varlen: prep_kernel then state_kernel, one gate per token-head"},
+                        "launch": "kda_gdn_prefill_varlen: as the KDA call, one gate per token-head"},
         "decode_pooled": {"ms": round(sum(pool_ms) / K, 5), "ms_min": round(min(pool_ms), 5),
                           "value": round(dbytes / (sum(pool_ms) / K * 1e-3) / 1e9, 1), "unit": "GB/s",
                           "pool_slots": 2 * dwl.num_seqs,
@@ -485,9 +601,13 @@ def main():
         "long_1m": long_rec,
         "backward": backward_report(bwd_ms, T, H, D),
         "roofline": dominant,
+        "ceilings": {"hbm_spec_GB_s": HBM_PEAK_GBPS, "copy_1GiB_GB_s": copy_gbps,
+                     "note": "copy = read + write bytes of a 1 GiB device-to-device copy, median of 10"},
     }
+    for rec in (varlen_rec, long_rec):
+        rec["frac_of_copy"] = round(rec["GB_s"] / copy_gbps, 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(P)
+        out["cpu_baseline"] = cpu_baseline(P, dev)
     print(json.dumps(out), flush=True)
 
 
