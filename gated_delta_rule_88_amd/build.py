@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_bf16.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.cpp", "kda_noalloc.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_bf16.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 
 

@@ -5,10 +5,6 @@
 
 #include <stdint.h>
 
-#include <atomic>
-
-#include <hip/hip_runtime.h>
-
 #include "kda_launch.h"
 
 namespace {
@@ -22,6 +18,10 @@ kda_status check_common(int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t
   if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
+
+}  // namespace
+
+namespace kda {
 
 // Checks of a prefill call's arguments other than the workspace.
 kda_status prefill_check(const void* q, const void* k, const void* v, const float* log_alpha, const void* beta,
@@ -39,15 +39,15 @@ kda_status prefill_check(const void* q, const void* k, const void* v, const floa
   return KDA_OK;
 }
 
-kda_status prefill_plain(const void* q, const void* k, const void* v,
+kda_status prefill_call(const void* q, const void* k, const void* v,
                               const float* log_alpha, const void* beta,
                               const int32_t* cu_seqlens, const float* init_state,
                               void* o, float* final_state, int32_t num_seqs,
                               int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                               kda_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, bool scalar_gate, bool raw) {
-  kda_status st = prefill_check(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
-                                total_tokens, num_heads, dk, dv, dtype);
+  kda_status st = kda::prefill_check(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
+                                     total_tokens, num_heads, dk, dv, dtype);
   if (st != KDA_OK) return st;
   if (workspace && !aligned16(workspace)) return KDA_ERR_ALIGN;
   const size_t need = kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype);
@@ -63,6 +63,10 @@ kda_status prefill_plain(const void* q, const void* k, const void* v,
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+}  // namespace kda
+
+namespace {
+using kda::prefill_call;
 
 kda_status decode_plain(const void* q, const void* k, const void* v, const float* log_alpha,
                            const void* beta, float* state, void* o, int32_t num_seqs,
@@ -129,7 +133,7 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
                               int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                               kda_dtype dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-  return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
+  return prefill_call(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
                        total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, false,
                        false);
 }
@@ -141,7 +145,7 @@ kda_status kda_gdn_prefill_varlen(const void* q, const void* k, const void* v,
                                   int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                                   kda_dtype dtype, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-  return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
+  return prefill_call(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
                        total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, true,
                        false);
 }
@@ -153,7 +157,7 @@ kda_status kda_prefill_varlen_raw(const void* q, const void* k, const void* v,
                                   int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                                   kda_dtype dtype, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-  return prefill_plain(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state, o, final_state, num_seqs,
+  return prefill_call(q, k, v, log_alpha, beta_logit, cu_seqlens, init_state, o, final_state, num_seqs,
                        total_tokens, num_heads, dk, dv, dtype, workspace, workspace_bytes, stream, false,
                        true);
 }
@@ -272,49 +276,3 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
 
 }  // extern "C"
 
-// ---------------------------------------------------------------------------
-// Prefill without allocation.  Its workspace is a device array of this
-// library: each GPU that runs the library holds its own copy (at its own
-// address) until the process ends.  In host code the array's name is only a
-// host-side stand-in, so the device address is looked up with
-// hipGetSymbolAddress, once per device with that device current, and only
-// that address is ever passed on (to the kernels, as the workspace).
-// ---------------------------------------------------------------------------
-static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
-
-namespace {
-constexpr int kMaxDevices = 64;
-std::atomic<void*> g_scratch_addr[kMaxDevices];   // per device; set once, never changed
-
-kda_status scratch_address(void** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
-  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
-  if (!p) {
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
-    g_scratch_addr[dev].store(p, std::memory_order_release);
-  }
-  *out = p;
-  return KDA_OK;
-}
-}  // namespace
-
-kda_status kda_prefill_varlen_noalloc(const void* q, const void* k, const void* v,
-                                      const float* log_alpha, const void* beta,
-                                      const int32_t* cu_seqlens, const float* init_state,
-                                      void* o, float* final_state, int32_t num_seqs,
-                                      int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
-                                      kda_dtype dtype, hipStream_t stream) {
-  kda_status st = prefill_check(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs,
-                                total_tokens, num_heads, dk, dv, dtype);
-  if (st != KDA_OK) return st;
-  void* ws = nullptr;
-  if (total_tokens > 0) {
-    if (kda_prefill_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, dtype) > KDA_NOALLOC_SCRATCH_BYTES)
-      return KDA_ERR_SCRATCH;
-    st = scratch_address(&ws);
-    if (st != KDA_OK) return st;
-  }
-  return prefill_plain(q, k, v, log_alpha, beta, cu_seqlens, init_state, o, final_state, num_seqs, total_tokens,
-                       num_heads, dk, dv, dtype, ws, KDA_NOALLOC_SCRATCH_BYTES, stream, false, false);
-}

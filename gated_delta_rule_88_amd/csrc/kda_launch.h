@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 struct DecodeArgs {
@@ -75,6 +77,18 @@ int64_t prefill_num_slots(int32_t num_seqs, int64_t total_tokens);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+
+// The prefill behind every plain prefill entry point (kda_api.cpp): checks of
+// the arguments other than the workspace, then the whole checked call.
+kda_status prefill_check(const void* q, const void* k, const void* v, const float* log_alpha, const void* beta,
+                         const int32_t* cu_seqlens, const float* init_state, void* o, float* final_state,
+                         int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                         kda_dtype dtype);
+kda_status prefill_call(const void* q, const void* k, const void* v, const float* log_alpha, const void* beta,
+                        const int32_t* cu_seqlens, const float* init_state, void* o, float* final_state,
+                        int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                        kda_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        bool scalar_gate, bool raw);
 
 // Backward: workspace bytes per (chunk slot, head) and the launcher.
 size_t backward_block_bytes(int d);

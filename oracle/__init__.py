@@ -52,16 +52,18 @@ _lock = threading.Lock()
 _lib = None
 
 
-def build(src: str = _SRC, out: str = _LIB_PATH, force: bool = False, grad_src: str = _GRAD_SRC) -> str:
+def build(src: str = _SRC, out: str = _LIB_PATH, force: bool = False, grad_src: str = _GRAD_SRC,
+          extra_flags=()) -> str:
     """Compile the oracle (forward ``src`` and gradient ``grad_src``) with gcc
-    (fp64, -O2, no fast-math) into ``out``."""
+    (fp64, -O2, no fast-math) into ``out``; ``extra_flags`` (e.g. sanitizer
+    instrumentation for the sanitizer tests) are added to the command."""
     if (not force and os.path.exists(out)
             and os.path.getmtime(out) >= max(os.path.getmtime(src), os.path.getmtime(grad_src))):
         return out
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-           "-fno-fast-math", "-ffp-contract=off", src, grad_src, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *extra_flags, src, grad_src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -73,7 +75,9 @@ def load(path: str | None = None):
     with _lock:
         if path is None and _lib is not None:
             return _lib
-        p = path or build()
+        # KDA_ORACLE_LIB: a separately built copy (the sanitizer tests run the
+        # pins against instrumented builds in child processes)
+        p = path or os.environ.get("KDA_ORACLE_LIB") or build()
         lib = ctypes.CDLL(p)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         lib.kda_oracle_prefill.restype = i32
