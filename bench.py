@@ -60,7 +60,8 @@ COPY_BYTES = 1 << 30
 
 
 # the device code of the kernels whose memory counters the traffic record holds
-TRAFFIC_SOURCES = ("kda_prefill_bf16.hip", "kda_decode.hip", "kda_device.h", "kda_prefill_common.h")
+TRAFFIC_SOURCES = ("kda_prefill_bf16.hip", "kda_decode.hip", "kda_backward.hip", "kda_device.h",
+                   "kda_prefill_common.h")
 
 
 def source_digest() -> str:
@@ -255,7 +256,8 @@ def stored_traffic():
 # kernels read from each part's run
 PART_KERNELS = {"copy": {"copy": "copyBuffer"},
                 "prefill": {"prefill": "fused_kernel", "init": "fused_init_kernel"},
-                "decode": {"decode": "decode_step_kernel"}}
+                "decode": {"decode": "decode_step_kernel"},
+                "backward": {"bprep": "bwd_prep", "bfwd": "bwd_fwd", "bdstate": "bwd_dstate", "bgrad": "bwd_grad"}}
 
 
 def _counter_pass(counter, part, outdir):
@@ -284,7 +286,7 @@ def run_traffic(outdir):
     outdir = os.path.abspath(outdir)   # the passes run with /tmp as working directory
     os.makedirs(outdir, exist_ok=True)
     rec = {"source_sha": source_digest(), "unit": "KiB per dispatch", "commands": []}
-    for part in ("copy", "prefill", "decode"):
+    for part in ("copy", "prefill", "decode", "backward"):
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             vals, cmd = _counter_pass(counter, part, outdir)
             rec["commands"].append(cmd)
@@ -300,23 +302,27 @@ def run_traffic(outdir):
 
     rec["prefill_call_bytes"] = scaled("prefill") + scaled("init")
     rec["decode_call_bytes"] = scaled("decode")
+    rec["backward_call_bytes"] = sum(scaled(k) for k in ("bprep", "bfwd", "bdstate", "bgrad"))
     for path in (os.path.join(outdir, "traffic_record.json"), TRAFFIC_RECORD):
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as fh:
             json.dump(rec, fh, indent=1)
-    print(json.dumps({k: rec[k] for k in ("prefill_call_bytes", "decode_call_bytes", "copy_factor_fetch",
-                                          "copy_factor_write")}), flush=True)
+    print(json.dumps({k: rec[k] for k in ("prefill_call_bytes", "decode_call_bytes", "backward_call_bytes",
+                                          "copy_factor_fetch", "copy_factor_write")}), flush=True)
 
 
 # ---------------------------------------------------------------------------
-def backward_report(ms, T, H, D):
+def backward_report(ms, T, H, D, traffic):
     bbytes, bflops = backward_algorithmic(T, H, D, 1)
     avg = sum(ms) / len(ms)
     tf = bflops / (avg * 1e-3) / 1e12
+    moved = traffic.get("backward_call_bytes") if traffic else None
     return {"ms": round(avg, 5), "ms_min": round(min(ms), 5), "calls": len(ms),
             "tokens_per_s": round(T / (avg * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": round(moved) if moved else None,
+                         "traffic_GB_s": round(moved / (avg * 1e-3) / 1e9, 1) if moved else None,
                          "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
                          "hbm_frac": round(bbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
             "launch": "kda_prefill_backward: bwd_prep, bwd_fwd, bwd_dstate, bwd_grad (fp32 MFMA)"}
@@ -599,7 +605,7 @@ def main():
                           "launch": "kda_decode_step_pooled: decode_step_kernel with a slot map"},
         "varlen_16": varlen_rec,
         "long_1m": long_rec,
-        "backward": backward_report(bwd_ms, T, H, D),
+        "backward": backward_report(bwd_ms, T, H, D, traffic),
         "roofline": dominant,
         "ceilings": {"hbm_spec_GB_s": HBM_PEAK_GBPS, "copy_1GiB_GB_s": copy_gbps,
                      "note": "copy = read + write bytes of a 1 GiB device-to-device copy, median of 10"},

@@ -240,7 +240,7 @@ size_t kda_prefill_backward_workspace_size(int32_t num_seqs, int64_t total_token
   if (check_common(num_seqs, num_heads, dk, dv, dtype) != KDA_OK) return 0;
   if (total_tokens < 0 || total_tokens > INT32_MAX) return 0;
   const int64_t slots = kda::prefill_num_slots(num_seqs, total_tokens);
-  return (size_t)slots * (size_t)num_heads * kda::backward_block_bytes(dk);
+  return kda::backward_workspace_bytes(num_seqs, slots, num_heads, dk);
 }
 
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,

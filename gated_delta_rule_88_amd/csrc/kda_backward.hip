@@ -40,7 +40,18 @@
 //                 chunk and the gradient of the initial state;
 //   4. bwd_grad   one workgroup per (chunk, head): the per-chunk products and
 //                 the element-wise assembly of dq, dk, dv, dbeta, dlog_alpha.
-// Everything per chunk lives in a per-(chunk, head) block of the workspace.
+// The kernels run over windows of chunk slots.  Everything per chunk lives in
+// a per-(chunk, head) block of the window, except the state entering each
+// chunk (S0), which is kept for every chunk of the call (64 KiB per (chunk,
+// head) at d = 128, against about 1 MB for a block).  A forward sweep over
+// the windows (prep, forward pass) stores S0; a reverse sweep then, window by
+// window from the last, recomputes the window's blocks (prep and forward pass
+// again from the stored S0, the same bits; the last window's blocks are still
+// in place), runs the reverse pass with dL/dS carried between windows, and
+// assembles the window's gradients.  One window covers every slot when the
+// blocks fit the window budget.
+#include <algorithm>
+
 #include "kda_launch.h"
 #include "kda_prefill_common.h"
 
@@ -50,7 +61,8 @@ namespace bwd {
 constexpr int C = kChunk;
 
 // Per-(chunk, head) workspace block, in floats.  Row-major [rows][cols];
-// S0 and DS are stored like the states: [value column][key].  EG, EC, EGA,
+// DS (and the stored S0 of every chunk, outside the blocks) are stored like
+// the states: [value column][key].  EG, EC, EGA,
 // EAG hold e^G, e^(gC-G), e^(G-a), e^(a-G) and GAM e^gC, each evaluated in
 // fp64 and rounded once; DG (the gradient of the cumulative decay) is
 // accumulated in fp64.
@@ -64,10 +76,18 @@ struct Ws {
   static constexpr int64_t DG = 24 * CD;   // fp64 [C][D], two floats per element
   static constexpr int64_t A = 26 * CD, BQ = A + CC, T = BQ + CC, TB = T + CC, DBQ = TB + CC, DT = DBQ + CC,
                            X = DT + CC, DA = X + CC, DMA = DA + CC;
-  static constexpr int64_t S0 = DMA + CC, DS = S0 + DD;
+  static constexpr int64_t DS = DMA + CC;
   static constexpr int64_t BETA = DS + DD, DBQD = BETA + C, GAM = DBQD + C;
   static constexpr int64_t FLOATS = GAM + D;
   static_assert(FLOATS % 4 == 0, "blocks stay 16-byte aligned");
+};
+
+// A window of chunk slots [slot_lo, slot_hi) and the workspace regions.
+struct Win {
+  int64_t slot_lo, slot_hi;
+  float* blocks;   // block of (slot, head): blocks + ((slot - slot_lo) * H + head) * FLOATS
+  float* s0;       // [slots][H][dv][dk]: the state entering every chunk of the call
+  float* carry;    // [N][H][dv][dk]: dL/dS handed from a window to the one before it
 };
 
 // A strided fp32 matrix view: element (i, j) at p[i * rs + j * cs]; one of
@@ -326,19 +346,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_prep(const In* __restrict__ q
                                                      const In* __restrict__ v, const float* __restrict__ log_alpha,
                                                      const In* __restrict__ beta, const In* __restrict__ grad_o,
                                                      const int32_t* __restrict__ cu, int N, int H,
-                                                     float* __restrict__ ws) {
+                                                     const Win win) {
   using L = Ws<D>;
   __shared__ __align__(16) float lds[kGemmLds + 2 * C * C + C];
   float* sA = lds + kGemmLds;    // A
   float* sT = sA + C * C;        // T
   float* sBeta = sT + C * C;
 
-  const int64_t item = blockIdx.x, slot = item / H;
+  const int64_t item = blockIdx.x, slot = win.slot_lo + item / H;
   const int h = (int)(item % H);
   int n, len;
   int64_t t0;
   if (!decode_slot(cu, N, slot, n, t0, len)) return;
-  float* B = ws + item * L::FLOATS;
+  float* B = win.blocks + item * L::FLOATS;
   const int tid = threadIdx.x;
 
   // the chunk's log decays, staged in LDS by the whole workgroup (rows past
@@ -512,13 +532,21 @@ __device__ __forceinline__ bool slice_of(int N, int H, int& n, int& h, int& vt) 
   return true;
 }
 
+// The chunks [c_lo, c_hi) of a sequence whose slots lie in the window
+// (c_hi == c_lo when there are none).
+__device__ __forceinline__ void window_chunks(const Win& win, int64_t slot0, int nch, int& c_lo, int& c_hi) {
+  c_lo = (int)max<int64_t>(0, win.slot_lo - slot0);
+  c_hi = (int)max<int64_t>(c_lo, min<int64_t>(nch, win.slot_hi - slot0));
+}
+
 // ---------------------------------------------------------------------------
-// Kernel 2: forward state pass, storing S0 and E of every chunk.
+// Kernel 2: forward state pass over the window's chunks, storing S0 of every
+// chunk (and of the first chunk after the window) and E of the window's.
 // Wave w owns key tiles [KTW w, KTW (w+1)) of the slice and token tile w.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ cu, int N, int H,
-                                                    const float* __restrict__ init, float* __restrict__ ws) {
+                                                    const float* __restrict__ init, const Win win) {
   using L = Ws<D>;
   // LDS strides: W is read as the A operand over (token, key) pairs and Kc as
   // the A operand over (key, token) pairs; D + 2 and D + 16 make both reads
@@ -535,21 +563,30 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
   const int64_t bos = cu[n], eos = cu[n + 1];
   const int nch = (int)((eos - bos + C - 1) / C);
   const int64_t slot0 = bos / C + n;
+  int c_lo, c_hi;
+  window_chunks(win, slot0, nch, c_lo, c_hi);
+  if (c_lo >= c_hi) return;
+  // S0 of chunk c, [value column][key]
+  auto s0_of = [&](int c) { return win.s0 + ((slot0 + c) * H + h) * (int64_t)D * D + (int64_t)col * D; };
 
+  // the state entering the window: the initial state, or the one stored by
+  // the window before
   f32x4 S[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
     const int key0 = 16 * (w * KTW + kt) + 4 * g;
-    S[kt] = init ? *reinterpret_cast<const f32x4*>(init + (((int64_t)n * H + h) * D + col) * D + key0)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c_lo > 0) S[kt] = *reinterpret_cast<const f32x4*>(s0_of(c_lo) + key0);
+    else S[kt] = init ? *reinterpret_cast<const f32x4*>(init + (((int64_t)n * H + h) * D + col) * D + key0)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  auto block = [&](int c) { return win.blocks + ((slot0 + c - win.slot_lo) * H + h) * L::FLOATS; };
   // the next chunk's operands are loaded into registers while this chunk is
   // computed: W and Kc (NQ quads each per thread), this lane's U and e^gC
   constexpr int NQ = C * D / 4 / kThreads;
   f32x4 pw[NQ], pk[NQ], pg[KTW];
   float pu[4];
   auto fetch = [&](int c) {
-    const float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+    const float* B = block(c);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
@@ -561,9 +598,9 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
   };
-  if (nch > 0) fetch(0);
-  for (int c = 0; c < nch; ++c) {
-    float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+  fetch(c_lo);
+  for (int c = c_lo; c < c_hi; ++c) {
+    float* B = block(c);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
@@ -580,11 +617,11 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt) + 4 * g;
-      *reinterpret_cast<f32x4*>(B + L::S0 + (int64_t)col * D + key0) = S[kt];
+      *reinterpret_cast<f32x4*>(s0_of(c) + key0) = S[kt];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(key0 + i) * 16 + l16] = S[kt][i];
     }
-    if (c + 1 < nch) fetch(c + 1);
+    if (c + 1 < c_hi) fetch(c + 1);
     __syncthreads();
     // E = U - W S for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -608,16 +645,23 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
     }
     __syncthreads();
   }
+  // the state entering the next window's first chunk of this sequence
+  if (c_hi < nch) {
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt)
+      *reinterpret_cast<f32x4*>(s0_of(c_hi) + 16 * (w * KTW + kt) + 4 * g) = S[kt];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: reverse pass over the chunks for dL/dS; stores dS_end and dE of
-// every chunk and dL/dS_0 of the sequence.
+// Kernel 3: reverse pass over the window's chunks for dL/dS; stores dS_end
+// and dE of each, hands dL/dS to the window before (carry) or, at the
+// sequence's first chunk, writes dL/dS_0.  A sequence without chunks is
+// handled by the first window (the last reverse pass to run).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict__ cu, int N, int H,
-                                                       const float* grad_final, float* grad_init,
-                                                       float* __restrict__ ws) {
+                                                       const float* grad_final, float* grad_init, const Win win) {
   // grad_init may be the grad_final buffer (in-place): each element is read
   // before the same thread writes it, so the two are not declared restrict
   using L = Ws<D>;
@@ -640,19 +684,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
   const int nch = (int)((eos - bos + C - 1) / C);
   const int64_t slot0 = bos / C + n;
   const int64_t sbase = (((int64_t)n * H + h) * D + col) * D;
+  int c_lo, c_hi;
+  window_chunks(win, slot0, nch, c_lo, c_hi);
+  if (nch > 0 ? c_lo >= c_hi : win.slot_lo != 0) return;
 
+  // dL/dS after the window: the upstream final-state gradient, or what the
+  // window after handed over
   f32x4 dS[KTW];
 #pragma unroll
   for (int kt = 0; kt < KTW; ++kt) {
     const int key0 = 16 * (w * KTW + kt) + 4 * g;
-    dS[kt] = grad_final ? *reinterpret_cast<const f32x4*>(grad_final + sbase + key0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c_hi < nch) dS[kt] = *reinterpret_cast<const f32x4*>(win.carry + sbase + key0);
+    else dS[kt] = grad_final ? *reinterpret_cast<const f32x4*>(grad_final + sbase + key0) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  auto block = [&](int c) { return win.blocks + ((slot0 + c - win.slot_lo) * H + h) * L::FLOATS; };
   // the previous chunk's operands are loaded into registers while this one
   // is computed
   constexpr int NQ = C * D / 4 / kThreads, NB = C * C / 4 / kThreads;
   f32x4 pb[NB], pk[NQ], pq[NQ], pw[NQ], po, pg[KTW];
   auto fetch = [&](int c) {
-    const float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+    const float* B = block(c);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
@@ -669,9 +720,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
   };
-  if (nch > 0) fetch(nch - 1);
-  for (int c = nch - 1; c >= 0; --c) {
-    float* B = ws + ((slot0 + c) * H + h) * L::FLOATS;
+  if (c_hi > c_lo) fetch(c_hi - 1);
+  for (int c = c_hi - 1; c >= c_lo; --c) {
+    float* B = block(c);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
@@ -696,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) sdS[(key0 + i) * 16 + l16] = dS[kt][i];
     }
-    if (c > 0) fetch(c - 1);
+    if (c > c_lo) fetch(c - 1);
     __syncthreads();
     // dE = Bq^T dO + Kc dS for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -724,11 +775,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
     }
     __syncthreads();
   }
-  if (grad_init) {
+  float* dst = c_lo > 0 ? win.carry : grad_init;
+  if (dst) {
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt) + 4 * g;
-      *reinterpret_cast<f32x4*>(grad_init + sbase + key0) = dS[kt];
+      *reinterpret_cast<f32x4*>(dst + sbase + key0) = dS[kt];
     }
   }
 }
@@ -738,17 +790,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restrict__ cu, int N, int H,
-                                                     float* __restrict__ ws, float* __restrict__ gq,
+                                                     const Win win, float* __restrict__ gq,
                                                      float* __restrict__ gk, float* __restrict__ gv,
                                                      float* __restrict__ gla, float* __restrict__ gbeta) {
   using L = Ws<D>;
   __shared__ __align__(16) float lds[kGemmLds];
-  const int64_t item = blockIdx.x, slot = item / H;
+  const int64_t item = blockIdx.x, slot = win.slot_lo + item / H;
   const int h = (int)(item % H);
   int n, len;
   int64_t t0;
   if (!decode_slot(cu, N, slot, n, t0, len)) return;
-  float* B = ws + item * L::FLOATS;
+  float* B = win.blocks + item * L::FLOATS;
+  const float* S0 = win.s0 + (slot * H + h) * (int64_t)D * D;   // [value column][key]
   const float* beta = B + L::BETA;
   double* dG = reinterpret_cast<double*>(B + L::DG);
   auto at = [&](int64_t base, int r, int c) -> float& { return B[base + (int64_t)r * D + c]; };
@@ -766,7 +819,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     EpiD e;
     e.x = F(L::DQ); e.fx = F(L::EG);
     e.dg = dG; e.fg = F(L::QG);
-    gemm_d<D>(M(L::DOX, D, 1), M(L::S0, D, 1), D, kNoMat, kNoMat, 0, lds, e);
+    gemm_d<D>(M(L::DOX, D, 1), Mat{S0, D, 1}, D, kNoMat, kNoMat, 0, lds, e);
   }
   {  // dQa = dBs Kb: dQ += dQa e^(G-a), dG += dQa o Qa
     EpiD e;
@@ -784,7 +837,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
   {  // dW = -dE S0^T
     EpiD e;
     e.store = F(L::DW); e.store_scale = -1.f;
-    gemm_d<D>(M(L::DE, D, 1), M(L::S0, D, 1), D, kNoMat, kNoMat, 0, lds, e);
+    gemm_d<D>(M(L::DE, D, 1), Mat{S0, D, 1}, D, kNoMat, kNoMat, 0, lds, e);
   }
   {  // P = T^T dE: dV = Diag(beta) P
     EpiD e;
@@ -844,7 +897,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     double dgam = 0.0, dkc = 0.0;
 #pragma unroll 16
     for (int j = grp * JG; j < (grp + 1) * JG; ++j)
-      dgam += (double)B[L::DS + (int64_t)j * D + c] * (double)B[L::S0 + (int64_t)j * D + c];
+      dgam += (double)B[L::DS + (int64_t)j * D + c] * (double)S0[(int64_t)j * D + c];
 #pragma unroll 16
     for (int r = grp * RG; r < (grp + 1) * RG; ++r) dkc += (double)at(L::DKC, r, c) * (double)at(L::KC, r, c);
     // partial of dgC = rowsum(dS_end o S0) gamma + colsum(dKc o Kc)
@@ -901,39 +954,83 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
   }
 }
 
+// Window budget: at most 512 chunk slots and 8 GiB of blocks per window (the
+// 8K workload at H = 32, 130 slots of 4.3 GB, is one window).
+constexpr int64_t kWindowSlots = 512;
+constexpr size_t kWindowBytes = (size_t)8 << 30;
+
+template <int D>
+static int64_t window_slots(int64_t slots, int H) {
+  const int64_t by_bytes = (int64_t)(kWindowBytes / ((size_t)H * Ws<D>::FLOATS * sizeof(float)));
+  return std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(slots, kWindowSlots), by_bytes));
+}
+
+// Workspace: the window's blocks, S0 of every chunk slot, the carry.
+template <int D>
+static size_t workspace_bytes_t(int32_t N, int64_t slots, int H) {
+  return ((size_t)window_slots<D>(slots, H) * H * Ws<D>::FLOATS + (size_t)slots * H * D * D +
+          (size_t)N * H * D * D) * sizeof(float);
+}
+
 template <int D, class In>
 static hipError_t launch_t(const BackwardArgs& A, hipStream_t stream) {
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
-  const int64_t items = slots * A.num_heads;
-  float* ws = (float*)A.workspace;
-  if (A.total_tokens > 0) {
-    hipLaunchKernelGGL((bwd_prep<D, In>), dim3((unsigned)items), dim3(kThreads), 0, stream, (const In*)A.q,
-                       (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, (const In*)A.grad_o,
-                       A.cu_seqlens, A.num_seqs, A.num_heads, ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const int H = A.num_heads;
+  const int64_t wsl = window_slots<D>(slots, H);
+  float* base = (float*)A.workspace;
+  Win win{0, 0, base, nullptr, nullptr};
+  if (base) {
+    win.s0 = base + wsl * H * Ws<D>::FLOATS;
+    win.carry = win.s0 + slots * H * (int64_t)D * D;
   }
-  const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
+  const int64_t pairs = (int64_t)A.num_seqs * H;
   const unsigned blocks = (unsigned)(((pairs + 7) / 8) * 8 * (D / 16));
-  if (A.total_tokens > 0) {
-    hipLaunchKernelGGL((bwd_fwd<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
-                       A.num_heads, A.init_state, ws);
+  auto dstate = [&]() {
+    hipLaunchKernelGGL((bwd_dstate<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs, H,
+                       A.grad_final_state, A.grad_init_state, win);
+    return hipGetLastError();
+  };
+  if (A.total_tokens == 0) return dstate();   // no chunks: dL/dS_0 = dL/dS_T
+  auto prep_fwd = [&]() {
+    const unsigned items = (unsigned)((win.slot_hi - win.slot_lo) * H);
+    hipLaunchKernelGGL((bwd_prep<D, In>), dim3(items), dim3(kThreads), 0, stream, (const In*)A.q, (const In*)A.k,
+                       (const In*)A.v, A.log_alpha, (const In*)A.beta, (const In*)A.grad_o, A.cu_seqlens, A.num_seqs,
+                       H, win);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_fwd<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs, H,
+                       A.init_state, win);
+    return hipGetLastError();
+  };
+  const int64_t nwin = (slots + wsl - 1) / wsl;
+  auto select = [&](int64_t w) {
+    win.slot_lo = w * wsl;
+    win.slot_hi = std::min<int64_t>(slots, win.slot_lo + wsl);
+  };
+  hipError_t e = hipSuccess;
+  for (int64_t w = 0; w < nwin && e == hipSuccess; ++w) {   // forward sweep: S0 of every chunk
+    select(w);
+    e = prep_fwd();
   }
-  hipLaunchKernelGGL((bwd_dstate<D>), dim3(blocks), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
-                     A.num_heads, A.grad_final_state, A.grad_init_state, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || A.total_tokens == 0) return e;
-  hipLaunchKernelGGL((bwd_grad<D>), dim3((unsigned)items), dim3(kThreads), 0, stream, A.cu_seqlens, A.num_seqs,
-                     A.num_heads, ws, A.grad_q, A.grad_k, A.grad_v, A.grad_log_alpha, A.grad_beta);
-  return hipGetLastError();
+  for (int64_t w = nwin - 1; w >= 0 && e == hipSuccess; --w) {   // reverse sweep
+    select(w);
+    if (w != nwin - 1) e = prep_fwd();   // the last window's blocks are still in place
+    if (e == hipSuccess) e = dstate();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((bwd_grad<D>), dim3((unsigned)((win.slot_hi - win.slot_lo) * H)), dim3(kThreads), 0, stream,
+                         A.cu_seqlens, A.num_seqs, H, win, A.grad_q, A.grad_k, A.grad_v, A.grad_log_alpha,
+                         A.grad_beta);
+      e = hipGetLastError();
+    }
+  }
+  return e;
 }
 
 }  // namespace bwd
 
-size_t backward_block_bytes(int d) {
-  return (d == 128 ? bwd::Ws<128>::FLOATS : bwd::Ws<64>::FLOATS) * sizeof(float);
+size_t backward_workspace_bytes(int32_t num_seqs, int64_t slots, int num_heads, int d) {
+  return d == 128 ? bwd::workspace_bytes_t<128>(num_seqs, slots, num_heads)
+                  : bwd::workspace_bytes_t<64>(num_seqs, slots, num_heads);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {

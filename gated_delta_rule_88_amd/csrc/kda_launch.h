@@ -90,8 +90,8 @@ kda_status prefill_call(const void* q, const void* k, const void* v, const float
                         kda_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
                         bool scalar_gate, bool raw);
 
-// Backward: workspace bytes per (chunk slot, head) and the launcher.
-size_t backward_block_bytes(int d);
+// Backward: workspace bytes for a call and the launcher.
+size_t backward_workspace_bytes(int32_t num_seqs, int64_t slots, int num_heads, int d);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace kda

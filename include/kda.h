@@ -309,9 +309,14 @@ kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v,
  *   grad_init_state  [N, H, dv, dk] fp32, or NULL (not written); it may be
  *                    the same buffer as grad_final_state, no other aliasing
  *   workspace        >= kda_prefill_backward_workspace_size(...) bytes of
- *                    device memory, contents irrelevant on entry (it holds
- *                    every chunk's factors and both state passes, about
- *                    0.96 MiB per (64-token chunk, head) at dk = 128)
+ *                    device memory, contents irrelevant on entry.  It holds
+ *                    the state entering every 64-token chunk (64 KiB per
+ *                    (chunk, head) at dk = 128), one dL/dS per (sequence,
+ *                    head), and the full factors of a window of at most 512
+ *                    chunk slots and 8 GiB (1.07 MB per (chunk, head)); longer
+ *                    calls run window by window, recomputing each window's
+ *                    factors once more (17.5 GB for 16 sequences of 270,810
+ *                    tokens at 32 heads, 25.8 GB for 2^20 tokens at 16).
  * Gradients are fp32 whatever `dtype` is.  Zero-length sequences give
  * grad_init_state = grad_final_state.  Errors as for kda_prefill_varlen.
  */

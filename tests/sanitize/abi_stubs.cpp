@@ -24,7 +24,9 @@ hipError_t clear_prefill_status(int*, hipStream_t) { ++g_launches; return hipSuc
 hipError_t launch_decode(const DecodeArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_f32(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill_bf16(const PrefillArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
-size_t backward_block_bytes(int d) { return d == 128 ? 1131520 : 300000; }
+size_t backward_workspace_bytes(int32_t num_seqs, int64_t slots, int num_heads, int d) {
+  return ((size_t)slots * num_heads + num_seqs) * d * d * 4 + (size_t)4 * num_heads * 300000;
+}
 hipError_t launch_backward(const BackwardArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 
 }  // namespace kda

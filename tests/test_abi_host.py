@@ -158,10 +158,26 @@ def test_decode_pooled_zero_sequences_is_a_no_op(lib):
 
 def test_backward_workspace_size(lib):
     f = lib.kda_prefill_backward_workspace_size
-    # per (chunk slot, head): 24 fp32 [64 x d] matrices, one fp64 [64 x d], 9 fp32
-    # [64 x 64], two [d x d] state blocks and the beta, diag(dBq), e^gC vectors
-    block_128 = 4 * (26 * 64 * 128 + 9 * 64 * 64 + 2 * 128 * 128 + 2 * 64 + 128)
-    assert f(1, 8192, 32, 128, 128, BF16) == (8192 // 64 + 1 + 1) * 32 * block_128
+    # a window of per-(chunk slot, head) blocks -- 24 fp32 [64 x d] matrices, one
+    # fp64 [64 x d], 9 fp32 [64 x 64], the dS_end block [d x d] and the beta,
+    # diag(dBq), e^gC vectors -- of at most 512 slots and 8 GiB; then the state
+    # entering every chunk slot [d x d] and one [d x d] carry per (sequence, head)
+    block_128 = 4 * (26 * 64 * 128 + 9 * 64 * 64 + 128 * 128 + 2 * 64 + 128)
+    state = 4 * 128 * 128
+
+    def expect(n, t, h):
+        slots = t // 64 + n + 1
+        win = max(1, min(slots, 512, (8 << 30) // (h * block_128)))
+        return win * h * block_128 + slots * h * state + n * h * state
+
+    assert f(1, 8192, 32, 128, 128, BF16) == expect(1, 8192, 32) == 130 * 32 * (block_128 + state) + 32 * state
+    # the variable-length and long-context workloads fit a 288 GB device, at
+    # most 0.25 MB per (chunk slot, head)
+    for n, t, h in ((16, 270810, 32), (1, 1 << 20, 16)):
+        size = f(n, t, h, 128, 128, BF16)
+        assert size == expect(n, t, h)
+        assert size / ((t // 64 + n + 1) * h) <= 0.25e6
+    assert f(1, 256, 1, 64, 64, F32) > 0
     assert f(1, 256, 1, 64, 64, F32) > 0
     assert f(1, 100, 2, 96, 96, BF16) == 0
     assert f(1, 100, 2, 128, 128, 7) == 0

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from gated_delta_rule_88_amd import inputs, kda
-from tests.parity import TOL, row_rel_err, state_rel_err
+from tests.parity import TOL, record, row_rel_err, state_rel_err
 from tests.test_gpu_prefill import make_case
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +50,8 @@ def check(d, go, gf, tol, label, want_init=True):
     got, ref = run_both(d, go, gf, want_init)
     e = errors(got, ref)
     print(label + ": " + ", ".join(f"d{n} {x:.2e}" for n, x in e.items()) + f" (tol {tol:g})", flush=True)
+    record(label + " (max over dq dk dv dlog_alpha dbeta; dS0)", max(e[n] for n in NAMES),
+           e.get("init_state", 0.0), tol)
     assert all(x <= tol for x in e.values()), (label, e)
     return got
 
@@ -117,3 +119,20 @@ def test_backward_8k_full():
     d = inputs.prefill_inputs(inputs.WORKLOADS["prefill_8k"])
     go, gf = upstream(d, seed=461)
     check(d, go, gf, TOL[torch.bfloat16], "backward prefill_8k")
+
+
+def test_backward_varlen_64k_in_windows():
+    """eight packed sequences, 66,000+ tokens in all (one empty, one of 37
+    tokens), over 2 heads: about 1,050 chunk slots, so the backward runs as
+    three windows of at most 512 slots -- chunk-entry states kept for every
+    chunk, each earlier window's blocks recomputed in the reverse sweep and
+    dL/dS carried between windows; every gradient against the oracle"""
+    import numpy as np
+    rng = np.random.default_rng(440)
+    lengths = rng.integers(3000, 15000, size=8).tolist()
+    lengths[3], lengths[5] = 0, 37
+    lengths[-1] += max(0, 66000 - sum(lengths))
+    assert sum(lengths) >= 65536
+    d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=441)
+    go, gf = upstream(d, 442)
+    check(d, go, gf, TOL[torch.bfloat16], f"backward varlen {sum(lengths)} tokens in windows")
