@@ -11,8 +11,8 @@
 // Kernel 1 (prep) runs one workgroup of four waves per (chunk, head) item,
 // two workgroups per CU, each wave holding 16 tokens of the chunk in
 // registers.  Per item it produces, as MFMA fragments:
-// W, Q' and Kc^T (fp16 fragments), U and Bqk U (fp16 accumulator tiles) and
-// e^G[C-1].
+// W, Q' and Kc^T (fp16 fragments), U and (Bqk U)^T (fp16 accumulator tiles)
+// and e^G[C-1].
 //
 // Precision (fp32 accumulation throughout).  Inside the prep, an operand
 // whose bf16 rounding would show in the outputs is split into hi + lo bf16
@@ -88,7 +88,7 @@ struct Rec {
   static constexpr size_t QP = W + 4 * KB * FB;              // [4 token tiles][KB]          Q'
   static constexpr size_t KC = QP + 4 * KB * FB;             // [NT key tiles][2]            Kc^T
   static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f16x4
-  static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 8;  // same layout, Bqk U
+  static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 8;  // same tiles of (Bqk U)^T: token l%16, columns 4 (l/16) + e
   static constexpr size_t G = BU + (size_t)NT * 4 * 64 * 8;  // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
@@ -531,7 +531,7 @@ __device__ __forceinline__ void prep_item(
   __syncthreads();
 
   // ---- G: Q'^T = Qg^T - W^T Bqk^T (tiles (it, w)) -> record Q';
-  //      Bqk U (tiles (w, ct)) -> record -------------------------------------------
+  //      (Bqk U)^T (tiles (ct, w)) -> record ----------------------------------------
   HFrag qrec;   // two key tiles of Q', stored as one fragment
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
@@ -558,9 +558,9 @@ __device__ __forceinline__ void prep_item(
       if (pb >= npb) break;
       const Frag uh = reinterpret_cast<const Frag*>(lds + L::UX)[(ct * 2 + pb) * 64 + l];
       const Frag ul = reinterpret_cast<const Frag*>(lds + L::UX + NT * 2 * FB)[(ct * 2 + pb) * 64 + l];
-      mma(bu, bqH[pb], uh);
-      mma(bu, bqH[pb], ul);
-      mma(bu, bqL[pb], uh);
+      mma(bu, uh, bqH[pb]);   // operands swapped: the tile of (Bqk U)^T
+      mma(bu, ul, bqH[pb]);
+      mma(bu, uh, bqL[pb]);
     }
     HHalf bu16;
 #pragma unroll
@@ -649,30 +649,38 @@ __device__ __forceinline__ void load_ops(Ops<D, VT>& o, Rsrc rs, int w, int l, i
 // sets the status word and lets the pass run on with NaN outputs, so that no
 // wave can hang.
 constexpr int kSpinLimit = 1 << 21;
+constexpr int kLeadSpinLimit = 1 << 18;   // a prep item's wait for the pass to come within reach
 
 struct Sync {
   const int* flags;   // nullptr: records are complete before the pass starts
   int* status;
+  int* marks;         // non-null: set flag (slot, head) to kConsumed after each chunk step
 };
 
+// Flag value of a chunk whose step the state pass (its first value slice)
+// has finished; prep items that may run only a bounded number of chunks
+// ahead of the pass wait for it (any nonzero flag means published).
+constexpr int kConsumed = 2;
+
 // Readiness of the records a pass is about to load.  `upto` is the last
-// chunk known to be published; when chunk c is needed beyond it, lane i
-// polls chunk c + i % 16 (clamped to the last chunk) until chunk c is
-// published, and `upto` advances over the published run that starts at c.
-// A pass that trails the prep by more than 16 chunks thus polls once every
-// 16 steps, and one right behind it polls every step.  The acquire fence
-// keeps the record loads after the poll.
+// chunk known to be published, every earlier one included.  When chunk c is
+// needed beyond it, lane i polls chunk upto + 1 + i % 16 (clamped to the
+// last chunk) and `upto` advances over the published run that starts right
+// after it, until it reaches c.  (A run that started at c itself would say
+// nothing of the chunks between: chunks are published out of order.)  A
+// pass that trails the prep by more than 16 chunks thus polls once every 16
+// steps, and one right behind it polls every step.  The acquire fence keeps
+// the record loads after the poll.
 __device__ __forceinline__ void need_record(const Sync& sy, int64_t slot0, int H, int h, int c, int nch, int lane,
                                             int& upto, bool& failed) {
   if (!sy.flags || failed || c <= upto) return;
-  const int* f = sy.flags + (slot0 + min(c + (lane & 15), nch - 1)) * H + h;
   for (int spin = 0;; ++spin) {
+    const int first = upto + 1;
+    const int* f = sy.flags + (slot0 + min(first + (lane & 15), nch - 1)) * H + h;
     const int ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t mask = __ballot(ready != 0) & 0xFFFFull;
-    if (mask & 1) {
-      upto = c + __builtin_ctzll(~mask) - 1;   // chunks c .. upto are published
-      break;
-    }
+    upto = first + __builtin_ctzll(~mask) - 1;   // chunks first .. upto are published
+    if (upto >= c) break;
     if (spin >= kSpinLimit) {
       failed = true;
       if (lane == 0) __hip_atomic_fetch_or(sy.status, kStatusWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -733,6 +741,10 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
       S[t][kt] = init ? *reinterpret_cast<const f32x4*>(init + (sbase + col) * D + 16 * kti + 4 * g)
                       : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  // The initial state is in registers before any record load is issued: a
+  // load still in flight into S at the loop head would make the compiler
+  // wait there for every load, at every iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   auto rec_of = [&](int c) {
     return rec_rsrc(ws + ((size_t)(slot0 + min(c, nch - 1)) * H + h) * R::BYTES, R::BYTES);
@@ -741,9 +753,11 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
   int upto = -1;          // last chunk whose record is known to be published
 
   // one chunk step with operands `ops`; meanwhile the operands of a later
-  // chunk (record `nrs`) are loaded into `nxt`, one part per phase
-  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, Rsrc nrs) {
-    need_record(sy, slot0, H, h, c + NB - 1, nch, l, upto, failed);
+  // chunk (record `nrs`) are loaded into `nxt`, one part per phase, once
+  // the records up to chunk `need` are known to be published (need < 0:
+  // an earlier step made sure of it)
+  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, Rsrc nrs, int need) {
+    if (need >= 0) need_record(sy, slot0, H, h, need, nch, l, upto, failed);
     load_ops_part<D, VT>(nxt, nrs, 0, w, l, g, vt0);
     const int64_t t0 = bos + (int64_t)c * kChunk;
     const int len = (int)min<int64_t>(kChunk, eos - t0);
@@ -791,30 +805,39 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
 #pragma unroll
         for (int p = 0; p < 2; ++p) mma(S[t][kt], ops.kc[kt][p], sE[t][p][l]);
       }
-    // O = Q' S + Bqk U for token tile w: off the state's dependency chain
+    // O^T = S^T Q'^T + (Bqk U)^T for token tile w, off the state's
+    // dependency chain.  The operands swapped in the product give the
+    // transposed tile: lane l holds token 16 w + l % 16 and four adjacent
+    // value columns, stored as one 8-byte write.
+    const int r = 16 * w + l16;
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-      f32x4 qsum;
+      f32x4 ot;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qsum[e] = (float)ops.bu[t][e];
+      for (int e = 0; e < 4; ++e) ot[e] = (float)ops.bu[t][e];
 #pragma unroll
-      for (int p = 0; p < KB; ++p) mma(qsum, ops.qp[p], HOLD_SF ? sf[HOLD_SF ? t : 0][p] : sSc[t][p][l]);
-      const int col = 16 * (vt0 + t) + l16;
+      for (int p = 0; p < KB; ++p) mma(ot, HOLD_SF ? sf[HOLD_SF ? t : 0][p] : sSc[t][p][l], ops.qp[p]);
+      Half ob;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * g + e;
-        if (r < len) o[((t0 + r) * H + h) * D + col] = (In)(failed ? __builtin_nanf("") : qsum[e]);
-      }
+      for (int e = 0; e < 4; ++e) ob[e] = (In)(failed ? __builtin_nanf("") : ot[e]);
+      if (r < len) *reinterpret_cast<Half*>(o + ((t0 + r) * H + h) * D + 16 * (vt0 + t) + 4 * g) = ob;
     }
+    if (sy.marks && tid == 0)
+      __hip_atomic_store(sy.marks + (slot0 + c) * H + h, kConsumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // Operand buffers in rotation: while chunk c is computed, the operands of
   // the next NB - 1 chunks are in flight (past the last chunk the last
   // record is read again, so every step issues the same loads and the
-  // compiler's waits stay exact).  Twelve steps per loop iteration: at the
-  // loop head the compiler waits for most loads in flight, so the head is
-  // reached once every twelve chunks rather than every NB.  (The one-launch
-  // path checks that a record is published before the step that loads it.)
+  // compiler's waits stay exact).  Twelve steps per loop iteration, a
+  // multiple of NB, so that the buffers hold the same roles at every loop
+  // head; the iterations have no early exit, and the last nch % 12 chunks
+  // run after the loop: an exit edge into the loop's latch would make the
+  // compiler wait there for every load in flight.  The one-launch path
+  // checks that a record is published before the step that loads it; in the
+  // loop the last step of an iteration checks one chunk further for the
+  // first step of the next, so that no wait for the producers sits at the
+  // loop head (the compiler then drains every load in flight there too).
   Ops<D, VT> bufA, bufB, bufC;
   if (nch > 0) {
     need_record(sy, slot0, H, h, 0, nch, l, upto, failed);
@@ -823,31 +846,54 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
       need_record(sy, slot0, H, h, 1, nch, l, upto, failed);
       load_ops<D, VT>(bufB, rec_of(1), w, l, g, vt0);
     }
+    need_record(sy, slot0, H, h, NB - 1, nch, l, upto, failed);   // for the first step
   }
-  for (int c0 = 0; c0 < nch; c0 += 12) {
+  // step u of 12 in a loop iteration: the chunk to check before its loads
+  auto need_of = [&](int c, int u) { return u == 0 ? -1 : c + NB - 1 + (u == 11); };
+  int c0 = 0;
+  for (; c0 + 12 <= nch; c0 += 12) {
     if constexpr (NB == 3) {
 #pragma unroll
       for (int u = 0; u < 12; u += 3) {
-        const int c = c0 + u;
-        if (c >= nch) break;
-        step(bufA, c, bufC, rec_of(c + 2));
-        if (c + 1 >= nch) break;
-        step(bufB, c + 1, bufA, rec_of(c + 3));
-        if (c + 2 >= nch) break;
-        step(bufC, c + 2, bufB, rec_of(c + 4));
+        step(bufA, c0 + u, bufC, rec_of(c0 + u + 2), need_of(c0 + u, u));
+        step(bufB, c0 + u + 1, bufA, rec_of(c0 + u + 3), need_of(c0 + u + 1, u + 1));
+        step(bufC, c0 + u + 2, bufB, rec_of(c0 + u + 4), need_of(c0 + u + 2, u + 2));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < 12; u += 2) {
-        const int c = c0 + u;
-        if (c >= nch) break;
-        step(bufA, c, bufB, rec_of(c + 1));
-        if (c + 1 >= nch) break;
-        step(bufB, c + 1, bufA, rec_of(c + 2));
+        step(bufA, c0 + u, bufB, rec_of(c0 + u + 1), need_of(c0 + u, u));
+        step(bufB, c0 + u + 1, bufA, rec_of(c0 + u + 2), need_of(c0 + u + 1, u + 1));
       }
     }
   }
+  if constexpr (NB == 3) {
+#pragma unroll
+    for (int u = 0; u < 12; u += 3) {
+      const int c = c0 + u;
+      if (c >= nch) break;
+      step(bufA, c, bufC, rec_of(c + 2), c + 2);
+      if (c + 1 >= nch) break;
+      step(bufB, c + 1, bufA, rec_of(c + 3), c + 3);
+      if (c + 2 >= nch) break;
+      step(bufC, c + 2, bufB, rec_of(c + 4), c + 4);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 12; u += 2) {
+      const int c = c0 + u;
+      if (c >= nch) break;
+      step(bufA, c, bufB, rec_of(c + 1), c + 1);
+      if (c + 1 >= nch) break;
+      step(bufB, c + 1, bufA, rec_of(c + 2), c + 2);
+    }
+  }
 
+  // The last steps loaded records past the end that are never used.  Wait
+  // for them here, once per pass: left in flight, they would make the
+  // compiler wait for every load at each loop head of the next pass that
+  // this workgroup runs.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (fin) {
 #pragma unroll
     for (int t = 0; t < VT; ++t)
@@ -891,8 +937,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   int pair, vt;
   task_of<NV>(blockIdx.x, gridDim.x, pair, vt);
   if (pair >= N * H) return;
-  state_task<D, VT, 3, true>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt, Sync{nullptr, nullptr},
-                             lds);
+  state_task<D, VT, 3, true>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt,
+                             Sync{nullptr, nullptr, nullptr}, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -947,7 +993,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
     const float* __restrict__ log_alpha, const In* __restrict__ beta, const int32_t* __restrict__ cu,
     int N, int H, const float* init, float* fin, In* __restrict__ o, unsigned char* __restrict__ ws,
     int* __restrict__ flags, FusedHdr* __restrict__ hdr, const int32_t* __restrict__ sidx, int pool_slots,
-    int nstate, int ntot) {
+    int nstate, int ntot, int lead) {
   constexpr int NV = D / (16 * VT);
   __shared__ __align__(16) unsigned char lds[FusedLds<D, VT>::BYTES];
   const int tid = threadIdx.x;
@@ -958,6 +1004,19 @@ __global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
     int n, len;
     int64_t t0;
     if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
+    if (lead > 0 && t0 - cu[n] >= (int64_t)lead * kChunk) {
+      // at most `lead` chunks ahead of the state pass of this head, so that
+      // the pass reads the record while the memory-side cache still holds
+      // it; a heuristic, so the wait is bounded and then simply ends
+      if (tid == 0) {
+        const int* f = flags + (slot - lead) * H + h;
+        for (int spin = 0; spin < kLeadSpinLimit; ++spin) {
+          if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kConsumed) break;
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      __syncthreads();
+    }
     prep_item<D, SCALAR, RAW>(q, k, v, log_alpha, beta, H, h, t0, len, ws + ((size_t)slot * H + h) * Rec<D>::BYTES,
                               lds, &hdr->status);
     // publish: every wave's record stores acknowledged, then the flag
@@ -968,11 +1027,11 @@ __global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
     return;
   }
   __shared__ int sTicket;
-  const Sync sy{flags, &hdr->status};
   int task = blockIdx.x;
   while (task < ntot) {
     int pair, vt;
     task_of<NV>(task, nstate, pair, vt);
+    const Sync sy{flags, &hdr->status, lead > 0 && vt == 0 ? flags : nullptr};
     if (pair < N * H)
       state_task<D, VT, FusedState<VT>::NB, FusedState<VT>::HOLD_SF>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H,
                                                                     pair % H, vt, sy, lds);
@@ -1027,6 +1086,9 @@ static hipError_t launch_two_kernel(const PrefillArgs& A, int vt, hipStream_t st
 #ifndef KDA_SLICE_TILES
 #define KDA_SLICE_TILES 0
 #endif
+#ifndef KDA_LEAD_CHUNKS
+#define KDA_LEAD_CHUNKS 30   // how far the prep may run ahead of a long pass
+#endif
 
 // Returns false (and launches nothing) when the device cannot hold enough
 // blocks at once for the one-launch path.
@@ -1044,6 +1106,17 @@ static bool launch_fused_vt(const PrefillArgs& A, int cus, hipStream_t stream, h
   const int64_t pairs = (int64_t)A.num_seqs * A.num_heads;
   const int ntasks = (int)(pairs * NV);
   const int nstate = (int)std::min<int64_t>((((int64_t)ntasks + 8 * NV - 1) / (8 * NV)) * (8 * NV), cap);
+  // Sequences that average 64K tokens or more, each pass in a block of its
+  // own from the start: the pass is the longer leg, and a prep left to run
+  // ahead writes records that are read back from HBM milliseconds later.
+  // Keeping it within KDA_LEAD_CHUNKS chunks of the pass lets the pass read
+  // them from the memory-side cache instead.  (2^20 tokens, 16 heads, d =
+  // 128: 22.0 ms unthrottled; a lead of 16, 24, 28, 30 chunks: 25.4, 19.4,
+  // 18.4, 18.2 ms; 32 and more: about 17.7 ms but now and then 23 to 25 ms.
+  // The prep's work per chunk is some 20 us, so a short lead starves the
+  // pass.)
+  const bool throttle = ntasks <= nstate && A.total_tokens >= (int64_t)A.num_seqs * 65536;
+  const int lead = throttle ? KDA_LEAD_CHUNKS : 0;
 
   const int64_t slots = prefill_num_slots(A.num_seqs, A.total_tokens);
   unsigned char* ws = (unsigned char*)A.workspace;
@@ -1057,7 +1130,7 @@ static bool launch_fused_vt(const PrefillArgs& A, int cus, hipStream_t stream, h
   hipLaunchKernelGGL(kern, dim3((unsigned)(nstate + items)), dim3(kPrepThreads), 0, stream, (const In*)A.q,
                      (const In*)A.k, (const In*)A.v, A.log_alpha, (const In*)A.beta, A.cu_seqlens, A.num_seqs,
                      A.num_heads, A.init_state, A.final_state, (In*)A.o, ws, flags, hdr, A.state_indices,
-                     A.pool_slots, nstate, std::max(nstate, ntasks));
+                     A.pool_slots, nstate, std::max(nstate, ntasks), lead);
   err = hipGetLastError();
   return true;
 }

@@ -96,6 +96,25 @@ def test_state_pass_slice_widths(nseq, H):
     check(d, TOL[torch.bfloat16], f"state pass slice width, {nseq} x {H} pairs")
 
 
+def test_long_sequences_with_bounded_prep_lead():
+    """two sequences of 70,000 and 66,000 tokens, 2 heads: sequences this long
+    (64K tokens or more on average) make the bf16 prep wait whenever it runs
+    more than a fixed number of chunks ahead of the state pass of its head;
+    outputs and final states on value columns 32..47 (columns of S never mix,
+    so the oracle on a column slice of v and of the initial state gives
+    exactly those columns)"""
+    lengths = [70000, 66000]
+    d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=497)
+    o, f = run_gpu(d)
+    cols = slice(32, 48)
+    ro, rf = oracle.prefill(d["q"], d["k"], d["v"][..., cols], d["log_alpha"], d["beta"],
+                            d["cu_seqlens"].long(), d["init_state"][:, :, cols, :])
+    eo, es = row_rel_err(o[..., cols], ro), state_rel_err(f[:, :, cols, :], rf)
+    _log(f"long sequences, bounded prep lead: o {eo:.3e} state {es:.3e}")
+    record("two long sequences, bounded prep lead (cols 32..47)", eo, es, TOL[torch.bfloat16])
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16-128", "f32-64"])
 def test_chunk_counts_around_the_loop_unroll(dtype, D):
     """sequences of 11, 12, 13, 24 and 25 chunks (full and partial last
