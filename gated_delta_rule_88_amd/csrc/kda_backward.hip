@@ -64,17 +64,19 @@ constexpr int C = kChunk;
 // DS (and the stored S0 of every chunk, outside the blocks) are stored like
 // the states: [value column][key].  EG, EC, EGA,
 // EAG hold e^G, e^(gC-G), e^(G-a), e^(a-G) and GAM e^gC, each evaluated in
-// fp64 and rounded once; DG (the gradient of the cumulative decay) is
-// accumulated in fp64.
+// fp64 and rounded once.  The key gradient is kept in two parts, DKP =
+// dKa e^(G-a) + dKg e^G and DKM = dKb e^(a-G) + dKc e^(gC-G): every
+// decay-scaled operand is an input times its factor, so the gradient of the
+// cumulative decay is dG = K o (DKP - DKM) + Q o DQ, formed in fp64 where it
+// is summed.
 template <int D>
 struct Ws {
   static constexpr int64_t CD = (int64_t)C * D, CC = (int64_t)C * C, DD = (int64_t)D * D;
   static constexpr int64_t KX = 0, QX = CD, VX = 2 * CD, DOX = 3 * CD, KA = 4 * CD, KB = 5 * CD, QA = 6 * CD,
                            KG = 7 * CD, QG = 8 * CD, KC = 9 * CD, EG = 10 * CD, EC = 11 * CD, EGA = 12 * CD,
                            EAG = 13 * CD, W = 14 * CD, U = 15 * CD, E = 16 * CD, DE = 17 * CD, DQ = 18 * CD,
-                           DK = 19 * CD, DKC = 20 * CD, DW = 21 * CD, P = 22 * CD, R = 23 * CD;
-  static constexpr int64_t DG = 24 * CD;   // fp64 [C][D], two floats per element
-  static constexpr int64_t A = 26 * CD, BQ = A + CC, T = BQ + CC, TB = T + CC, DBQ = TB + CC, DT = DBQ + CC,
+                           DKP = 19 * CD, DKC = 20 * CD, DW = 21 * CD, P = 22 * CD, R = 23 * CD, DKM = 24 * CD;
+  static constexpr int64_t A = 25 * CD, BQ = A + CC, T = BQ + CC, TB = T + CC, DBQ = TB + CC, DT = DBQ + CC,
                            X = DT + CC, DA = X + CC, DMA = DA + CC;
   static constexpr int64_t DS = DMA + CC;
   static constexpr int64_t BETA = DS + DD, DBQD = BETA + C, GAM = DBQD + C;
@@ -101,6 +103,21 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// The product helpers below are not inlined, so their pointer arguments
+// reach them without an address space, and the compiler would use flat
+// accesses (counted on both the vector-memory and the LDS counters, so
+// every wait covers both).  They state the space instead: workspace and
+// outputs are global memory, the panels and accumulators LDS.
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) const float gcfloat;
+typedef __attribute__((address_space(1))) const f32x4 gcf32x4;
+typedef __attribute__((address_space(3))) float lfloat;
+typedef __attribute__((address_space(3))) f32x4 lf32x4;
+__device__ __forceinline__ gfloat* glb(float* p) { return (gfloat*)p; }
+__device__ __forceinline__ gcfloat* glb(const float* p) { return (gcfloat*)p; }
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(gcf32x4*)p; }
+__device__ __forceinline__ lfloat* loc(float* p) { return (lfloat*)p; }
+
 // out (64 x N) = A (64 x Kd) B (Kd x N) by the whole workgroup (wave w owns
 // output rows [16 w, 16 w + 16)); Kd a multiple of 32.  Panels of 32
 // reduction indices are staged in LDS, reduction-index major, so that every
@@ -112,8 +129,8 @@ constexpr int kGemmLds = 32 * 80 + 32 * 144;   // floats, for N <= 128
 template <int N, class Epi>
 __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int Kd, float* lds, Epi epi) {
   constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
-  float* sA = lds;
-  float* sB = lds + 32 * LA;
+  lfloat* sA = loc(lds);
+  lfloat* sB = loc(lds) + 32 * LA;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
   f32x4 acc[N / 16];
 #pragma unroll
@@ -125,16 +142,14 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int idx = tid + 256 * it;
-      ra[it] = A.cs == 1
-                   ? *reinterpret_cast<const f32x4*>(A.p + (int64_t)(idx & 63) * A.rs + k0 + 4 * (idx >> 6))
-                   : *reinterpret_cast<const f32x4*>(A.p + (int64_t)(k0 + (idx >> 4)) * A.cs + 4 * (idx & 15));
+      ra[it] = A.cs == 1 ? ld4(A.p + (int64_t)(idx & 63) * A.rs + k0 + 4 * (idx >> 6))
+                         : ld4(A.p + (int64_t)(k0 + (idx >> 4)) * A.cs + 4 * (idx & 15));
     }
 #pragma unroll
     for (int it = 0; it < NBQ; ++it) {
       const int idx = tid + 256 * it;
-      rb[it] = B.cs == 1
-                   ? *reinterpret_cast<const f32x4*>(B.p + (int64_t)(k0 + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
-                   : *reinterpret_cast<const f32x4*>(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
+      rb[it] = B.cs == 1 ? ld4(B.p + (int64_t)(k0 + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                         : ld4(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
     }
   };
   __syncthreads();   // operands written just before by other threads are visible
@@ -148,14 +163,14 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) sA[(4 * kq + i) * LA + r] = ra[it][i];
       } else {           // row index contiguous
-        *reinterpret_cast<f32x4*>(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
+        *(lf32x4*)(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
       }
     }
 #pragma unroll
     for (int it = 0; it < NBQ; ++it) {
       const int idx = tid + 256 * it;
       if (B.cs == 1) {   // column index contiguous
-        *reinterpret_cast<f32x4*>(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+        *(lf32x4*)(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
       } else {           // reduction index contiguous
         const int n = idx % N, kq = idx / N;
 #pragma unroll
@@ -187,8 +202,8 @@ template <int N>
 __device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2, int K2,
                                       float* lds, f32x4 (&acc)[N / 16]) {
   constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
-  float* sA = lds;
-  float* sB = lds + 32 * LA;
+  lfloat* sA = loc(lds);
+  lfloat* sB = loc(lds) + 32 * LA;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
 #pragma unroll
   for (int nt = 0; nt < N / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -203,14 +218,14 @@ __device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const 
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int idx = tid + 256 * it;
-      ra[it] = a_kc ? *reinterpret_cast<const f32x4*>(A.p + (int64_t)(idx & 63) * A.rs + kk + 4 * (idx >> 6))
-                    : *reinterpret_cast<const f32x4*>(A.p + (int64_t)(kk + (idx >> 4)) * A.cs + 4 * (idx & 15));
+      ra[it] = a_kc ? ld4(A.p + (int64_t)(idx & 63) * A.rs + kk + 4 * (idx >> 6))
+                    : ld4(A.p + (int64_t)(kk + (idx >> 4)) * A.cs + 4 * (idx & 15));
     }
 #pragma unroll
     for (int it = 0; it < NBQ; ++it) {
       const int idx = tid + 256 * it;
-      rb[it] = b_nc ? *reinterpret_cast<const f32x4*>(B.p + (int64_t)(kk + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
-                    : *reinterpret_cast<const f32x4*>(B.p + (int64_t)(idx % N) * B.cs + kk + 4 * (idx / N));
+      rb[it] = b_nc ? ld4(B.p + (int64_t)(kk + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                    : ld4(B.p + (int64_t)(idx % N) * B.cs + kk + 4 * (idx / N));
     }
   };
   __syncthreads();
@@ -224,14 +239,14 @@ __device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) sA[(4 * (idx >> 6) + i) * LA + (idx & 63)] = ra[it][i];
       } else {
-        *reinterpret_cast<f32x4*>(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
+        *(lf32x4*)(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
       }
     }
 #pragma unroll
     for (int it = 0; it < NBQ; ++it) {
       const int idx = tid + 256 * it;
       if (b_nc) {
-        *reinterpret_cast<f32x4*>(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+        *(lf32x4*)(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sB[(4 * (idx / N) + i) * LB + idx % N] = rb[it][i];
@@ -252,13 +267,14 @@ __device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const 
 constexpr Mat kNoMat = {nullptr, 1, 1};
 
 // What the epilogue of a 64 x D product does with acc, the product (every
-// part optional; each array is row-major [C][D] in the workspace block):
+// part optional; store, out, x and fx are row-major [C][D] arrays of the
+// workspace block, or outputs, in global memory):
 //   store = acc * store_scale;  out[(row) * out_rs + col] = beta_row * acc
 //   for rows < len (the value gradient, straight into the output);
-//   x  = (x_add ? x : 0) + s_row * acc * fx;
-//   dg = (g_add ? dg : 0) + g_sign * s_row * acc * fg   (fp64, exact products)
-// with s_row = beta_row when row_beta, else 1.  Each part loads everything it
-// needs before its first store, so a lane keeps its loads in flight.
+//   x  = (x_add ? x : 0) + s_row * acc * fx
+// with s_row = beta_row when row_beta, else 1.  Each part loads everything
+// it needs (half a tile at a time) before its first store, so a lane keeps
+// its loads in flight.
 struct EpiD {
   float* store = nullptr;
   float store_scale = 1.f;
@@ -268,10 +284,6 @@ struct EpiD {
   float* x = nullptr;
   const float* fx = nullptr;
   bool x_add = false;
-  double* dg = nullptr;
-  const float* fg = nullptr;
-  bool g_add = false;
-  float g_sign = 1.f;
   bool row_beta = false;
   const float* beta = nullptr;
 };
@@ -282,56 +294,50 @@ __device__ __attribute__((noinline)) void gemm_d(const Mat A1, const Mat B1, int
   constexpr int NT = D / 16;
   f32x4 acc[NT];
   wg_mm<D>(A1, B1, K1, A2, B2, K2, lds, acc);
-  const int w = threadIdx.x >> 6, g = (threadIdx.x & 63) >> 4, l16 = threadIdx.x & 15;
+  const int tid = threadIdx.x, w = tid >> 6, g = (tid & 63) >> 4, l16 = tid & 15;
   const int64_t lane = (int64_t)(16 * w + 4 * g) * D + l16;   // this lane's first element
+  gcfloat* beta = glb(e.beta);
   float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = e.row_beta ? e.beta[16 * w + 4 * g + i] : 1.f;
+  for (int i = 0; i < 4; ++i) s[i] = e.row_beta ? beta[16 * w + 4 * g + i] : 1.f;
   if (e.store) {
+    gfloat* st = glb(e.store);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e.store[lane + i * D + 16 * nt] = e.store_scale * acc[nt][i];
+      for (int i = 0; i < 4; ++i) st[lane + i * D + 16 * nt] = e.store_scale * acc[nt][i];
   }
   if (e.out) {
+    gfloat* out = glb(e.out);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * g + i;
-      const float b = e.beta[r];
+      const float b = beta[r];
       if (r < e.len)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) e.out[r * e.out_rs + 16 * nt + l16] = b * acc[nt][i];
+        for (int nt = 0; nt < NT; ++nt) out[r * e.out_rs + 16 * nt + l16] = b * acc[nt][i];
     }
   }
+  constexpr int NH = NT > 4 ? NT / 2 : NT;   // the read-modify-write goes half a tile at a time
   if (e.x) {
-    f32x4 f[NT], x[NT];
+    gcfloat* fx = glb(e.fx);
+    gfloat* x = glb(e.x);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int n0 = 0; n0 < NT; n0 += NH) {
+      f32x4 f[NH], xv[NH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[nt][i] = e.fx[lane + i * D + 16 * nt];
-        x[nt][i] = e.x_add ? e.x[lane + i * D + 16 * nt] : 0.f;
-      }
+      for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+        for (int i = 0; i < 4; ++i) {
+          f[nt][i] = fx[lane + i * D + 16 * (n0 + nt)];
+          xv[nt][i] = e.x_add ? x[lane + i * D + 16 * (n0 + nt)] : 0.f;
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e.x[lane + i * D + 16 * nt] = x[nt][i] + s[i] * acc[nt][i] * f[nt][i];
-  }
-  if (e.dg) {
-    f32x4 f[NT];
-    double d[NT][4];
+      for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[nt][i] = e.fg[lane + i * D + 16 * nt];
-        d[nt][i] = e.g_add ? e.dg[lane + i * D + 16 * nt] : 0.0;
-      }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        e.dg[lane + i * D + 16 * nt] = d[nt][i] + (double)(e.g_sign * s[i] * acc[nt][i]) * (double)f[nt][i];
+        for (int i = 0; i < 4; ++i)
+          x[lane + i * D + 16 * (n0 + nt)] = xv[nt][i] + s[i] * acc[n0 + nt][i] * f[nt][i];
+    }
   }
 }
 
@@ -441,13 +447,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_prep(const In* __restrict__ q
   // (wg_gemm starts with a barrier)
 
   // A = strict_lower(Ka Kb^T), Bq = lower(Qa Kb^T)
-  wg_gemm<C>(Mat{B + L::KA, D, 1}, Mat{B + L::KB, 1, D}, D, lds, [&](int r, int s, float x) {
+  wg_gemm<C>(Mat{B + L::KA, D, 1}, Mat{B + L::KB, 1, D}, D, lds, [=](int r, int s, float x) {
     x = s < r ? x : 0.f;
-    B[L::A + r * C + s] = x;
-    sA[r * C + s] = x;
+    glb(B)[L::A + r * C + s] = x;
+    loc(sA)[r * C + s] = x;
   });
   wg_gemm<C>(Mat{B + L::QA, D, 1}, Mat{B + L::KB, 1, D}, D, lds,
-             [&](int r, int s, float x) { B[L::BQ + r * C + s] = s <= r ? x : 0.f; });
+             [=](int r, int s, float x) { glb(B)[L::BQ + r * C + s] = s <= r ? x : 0.f; });
 
   // T = (I + Diag(beta) A)^-1 = M^-1 (unit lower triangular), by 16 x 16
   // blocks: wave w inverts diagonal block w by substitution down its columns
@@ -513,9 +519,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_prep(const In* __restrict__ q
 
   // W = Tb Kg, U = Tb V
   wg_gemm<D>(Mat{B + L::TB, C, 1}, Mat{B + L::KG, D, 1}, C, lds,
-             [&](int r, int c, float x) { B[L::W + (int64_t)r * D + c] = x; });
+             [=](int r, int c, float x) { glb(B)[L::W + (int64_t)r * D + c] = x; });
   wg_gemm<D>(Mat{B + L::TB, C, 1}, Mat{B + L::VX, D, 1}, C, lds,
-             [&](int r, int c, float x) { B[L::U + (int64_t)r * D + c] = x; });
+             [=](int r, int c, float x) { glb(B)[L::U + (int64_t)r * D + c] = x; });
 }
 
 // (sequence, head, 16-column slice) of a workgroup; same XCD-aware order as
@@ -803,7 +809,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
   float* B = win.blocks + item * L::FLOATS;
   const float* S0 = win.s0 + (slot * H + h) * (int64_t)D * D;   // [value column][key]
   const float* beta = B + L::BETA;
-  double* dG = reinterpret_cast<double*>(B + L::DG);
   auto at = [&](int64_t base, int r, int c) -> float& { return B[base + (int64_t)r * D + c]; };
   auto M = [&](int64_t base, int rs, int cs) { return Mat{B + base, rs, cs}; };
   auto F = [&](int64_t base) { return B + base; };
@@ -811,27 +816,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
   // dBq = lower(dO E^T), kept as its strict lower part and its diagonal:
   // Bq[r][r] = q_r . k_r carries no decay, so its terms would enter dG twice
   // with opposite signs; they go straight to dq and dk instead
-  wg_gemm<C>(M(L::DOX, D, 1), M(L::E, 1, D), D, lds, [&](int r, int s, float x) {
-    B[L::DBQ + r * C + s] = s < r ? x : 0.f;
-    if (s == r) B[L::DBQD + r] = x;
+  wg_gemm<C>(M(L::DOX, D, 1), M(L::E, 1, D), D, lds, [=](int r, int s, float x) {
+    glb(B)[L::DBQ + r * C + s] = s < r ? x : 0.f;
+    if (s == r) glb(B)[L::DBQD + r] = x;
   });
-  {  // dQg = dO S0^T: dQ = dQg e^G, dG = dQg o Qg
+  {  // dQg = dO S0^T: dQ = dQg e^G
     EpiD e;
     e.x = F(L::DQ); e.fx = F(L::EG);
-    e.dg = dG; e.fg = F(L::QG);
     gemm_d<D>(M(L::DOX, D, 1), Mat{S0, D, 1}, D, kNoMat, kNoMat, 0, lds, e);
   }
-  {  // dQa = dBs Kb: dQ += dQa e^(G-a), dG += dQa o Qa
+  {  // dQa = dBs Kb: dQ += dQa e^(G-a)
     EpiD e;
     e.x = F(L::DQ); e.fx = F(L::EGA); e.x_add = true;
-    e.dg = dG; e.fg = F(L::QA); e.g_add = true;
     gemm_d<D>(M(L::DBQ, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
   }
-  {  // dKc = E dS_end^T: dK = dKc e^(gC-G), dG -= dKc o Kc
+  {  // dKc = E dS_end^T: dKm = dKc e^(gC-G)
     EpiD e;
     e.store = F(L::DKC);
-    e.x = F(L::DK); e.fx = F(L::EC);
-    e.dg = dG; e.fg = F(L::KC); e.g_add = true; e.g_sign = -1.f;
+    e.x = F(L::DKM); e.fx = F(L::EC);
     gemm_d<D>(M(L::E, D, 1), M(L::DS, D, 1), D, kNoMat, kNoMat, 0, lds, e);
   }
   {  // dW = -dE S0^T
@@ -845,11 +847,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     e.out = gv + (t0 * H + h) * D; e.out_rs = (int64_t)H * D; e.len = len; e.beta = beta;
     gemm_d<D>(M(L::T, 1, C), M(L::DE, D, 1), C, kNoMat, kNoMat, 0, lds, e);
   }
-  {  // R = T^T dW: dKg = Diag(beta) R: dK += dKg e^G, dG += dKg o Kg
+  {  // R = T^T dW: dKg = Diag(beta) R: dKp = dKg e^G
     EpiD e;
     e.store = F(L::R);
-    e.x = F(L::DK); e.fx = F(L::EG); e.x_add = true;
-    e.dg = dG; e.fg = F(L::KG); e.g_add = true;
+    e.x = F(L::DKP); e.fx = F(L::EG);
     e.row_beta = true; e.beta = beta;
     gemm_d<D>(M(L::T, 1, C), M(L::DW, D, 1), C, kNoMat, kNoMat, 0, lds, e);
   }
@@ -866,22 +867,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     }
   }
   // X = dT T^T; dM = -T^T X: dA = strict_lower(Diag(beta) dM), dMA = strict_lower(dM) o A
-  wg_gemm<C>(M(L::DT, C, 1), M(L::T, 1, C), C, lds, [&](int r, int s, float x) { B[L::X + r * C + s] = x; });
-  wg_gemm<C>(M(L::T, 1, C), M(L::X, C, 1), C, lds, [&](int r, int s, float x) {
+  wg_gemm<C>(M(L::DT, C, 1), M(L::T, 1, C), C, lds, [=](int r, int s, float x) { glb(B)[L::X + r * C + s] = x; });
+  wg_gemm<C>(M(L::T, 1, C), M(L::X, C, 1), C, lds, [=](int r, int s, float x) {
     const float dm = -x;
-    B[L::DA + r * C + s] = s < r ? beta[r] * dm : 0.f;
-    B[L::DMA + r * C + s] = s < r ? dm * B[L::A + r * C + s] : 0.f;
+    glb(B)[L::DA + r * C + s] = s < r ? glb(beta)[r] * dm : 0.f;
+    glb(B)[L::DMA + r * C + s] = s < r ? dm * glb(B)[L::A + r * C + s] : 0.f;
   });
-  {  // dKa = dA Kb: dK += dKa e^(G-a), dG += dKa o Ka
+  {  // dKa = dA Kb: dKp += dKa e^(G-a)
     EpiD e;
-    e.x = F(L::DK); e.fx = F(L::EGA); e.x_add = true;
-    e.dg = dG; e.fg = F(L::KA); e.g_add = true;
+    e.x = F(L::DKP); e.fx = F(L::EGA); e.x_add = true;
     gemm_d<D>(M(L::DA, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
   }
-  {  // dKb = dA^T Ka + dBs^T Qa: dK += dKb e^(a-G), dG -= dKb o Kb
+  {  // dKb = dA^T Ka + dBs^T Qa: dKm += dKb e^(a-G)
     EpiD e;
-    e.x = F(L::DK); e.fx = F(L::EAG); e.x_add = true;
-    e.dg = dG; e.fg = F(L::KB); e.g_add = true; e.g_sign = -1.f;
+    e.x = F(L::DKM); e.fx = F(L::EAG); e.x_add = true;
     gemm_d<D>(M(L::DA, 1, C), M(L::KA, D, 1), C, M(L::DBQ, 1, C), M(L::QA, D, 1), C, lds, e);
   }
   __syncthreads();
@@ -916,7 +915,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     double acc2 = 0.0;
 #pragma unroll
     for (int x = RG - 1; x >= 0; --x) {
-      acc2 += dG[(int64_t)(grp * RG + x) * D + c];
+      const int r = grp * RG + x;
+      acc2 += (double)at(L::KX, r, c) * ((double)at(L::DKP, r, c) - (double)at(L::DKM, r, c)) +
+              (double)at(L::QX, r, c) * (double)at(L::DQ, r, c);
       suf[x] = acc2;
     }
     __syncthreads();   // sRed partials consumed
@@ -931,7 +932,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
       const int r = grp * RG + x;
       const float dd = B[L::DBQD + r];
       const float gqv = at(L::DQ, r, c) + dd * at(L::KX, r, c);
-      const float gkv = at(L::DK, r, c) + dd * at(L::QX, r, c);
+      const float gkv = at(L::DKP, r, c) + at(L::DKM, r, c) + dd * at(L::QX, r, c);
       if (r < len) {
         const int64_t o = ((t0 + r) * H + h) * D + c;
         gla[o] = (float)(suf[x] + later);
