@@ -587,24 +587,37 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
   }
   auto block = [&](int c) { return win.blocks + ((slot0 + c - win.slot_lo) * H + h) * L::FLOATS; };
   // the next chunk's operands are loaded into registers while this chunk is
-  // computed: W and Kc (NQ quads each per thread), this lane's U and e^gC
+  // computed: W and Kc (NQ quads each per thread), this lane's U and e^gC,
+  // in two parts issued during the two products, so that the vector memory
+  // path works while the matrix cores do
   constexpr int NQ = C * D / 4 / kThreads;
   f32x4 pw[NQ], pk[NQ], pg[KTW];
   float pu[4];
-  auto fetch = [&](int c) {
+  auto fetch = [&](int c, int part) {
     const float* B = block(c);
+    if (part == 0) {
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
-      pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
-      pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
+      for (int i = 0; i < NQ; ++i) {
+        const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+        pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pu[i] = B[L::U + (int64_t)(16 * w + 4 * g + i) * D + col];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+        pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
+      }
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt)
+        pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pu[i] = B[L::U + (int64_t)(16 * w + 4 * g + i) * D + col];
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
   };
-  fetch(c_lo);
+  if (c_lo < c_hi) {
+    fetch(c_lo, 0);
+    fetch(c_lo, 1);
+  }
   for (int c = c_lo; c < c_hi; ++c) {
     float* B = block(c);
 #pragma unroll
@@ -627,8 +640,8 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) sS[(key0 + i) * 16 + l16] = S[kt][i];
     }
-    if (c + 1 < c_hi) fetch(c + 1);
     __syncthreads();
+    if (c + 1 < c_hi) fetch(c + 1, 0);
     // E = U - W S for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -641,6 +654,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
       sE[r * 16 + l16] = e;
     }
     __syncthreads();
+    if (c + 1 < c_hi) fetch(c + 1, 1);
     // S <- Diag(gamma) S + Kc^T E
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
@@ -705,28 +719,40 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
   }
   auto block = [&](int c) { return win.blocks + ((slot0 + c - win.slot_lo) * H + h) * L::FLOATS; };
   // the previous chunk's operands are loaded into registers while this one
-  // is computed
+  // is computed, in two parts issued during the two products, so that the
+  // vector memory path works while the matrix cores do
   constexpr int NQ = C * D / 4 / kThreads, NB = C * C / 4 / kThreads;
   f32x4 pb[NB], pk[NQ], pq[NQ], pw[NQ], po, pg[KTW];
-  auto fetch = [&](int c) {
+  auto fetch = [&](int c, int part) {
     const float* B = block(c);
+    if (part == 0) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
-      pb[i] = *reinterpret_cast<const f32x4*>(B + L::BQ + s * C + 4 * tq);
+      for (int i = 0; i < NB; ++i) {
+        const int idx = tid + kThreads * i, s = idx / (C / 4), tq = idx % (C / 4);
+        pb[i] = *reinterpret_cast<const f32x4*>(B + L::BQ + s * C + 4 * tq);
+      }
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+        pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
+      }
+      po = *reinterpret_cast<const f32x4*>(B + L::DOX + (int64_t)(tid >> 2) * D + 16 * vt + 4 * (tid & 3));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
+        pq[i] = *reinterpret_cast<const f32x4*>(B + L::QG + (int64_t)r * D + 4 * cq);
+        pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
+      }
+#pragma unroll
+      for (int kt = 0; kt < KTW; ++kt)
+        pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
     }
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int idx = tid + kThreads * i, r = idx / (D / 4), cq = idx % (D / 4);
-      pk[i] = *reinterpret_cast<const f32x4*>(B + L::KC + (int64_t)r * D + 4 * cq);
-      pq[i] = *reinterpret_cast<const f32x4*>(B + L::QG + (int64_t)r * D + 4 * cq);
-      pw[i] = *reinterpret_cast<const f32x4*>(B + L::W + (int64_t)r * D + 4 * cq);
-    }
-    po = *reinterpret_cast<const f32x4*>(B + L::DOX + (int64_t)(tid >> 2) * D + 16 * vt + 4 * (tid & 3));
-#pragma unroll
-    for (int kt = 0; kt < KTW; ++kt) pg[kt] = *reinterpret_cast<const f32x4*>(B + L::GAM + 16 * (w * KTW + kt) + 4 * g);
   };
-  if (c_hi > c_lo) fetch(c_hi - 1);
+  if (c_hi > c_lo) {
+    fetch(c_hi - 1, 0);
+    fetch(c_hi - 1, 1);
+  }
   for (int c = c_hi - 1; c >= c_lo; --c) {
     float* B = block(c);
 #pragma unroll
@@ -753,8 +779,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) sdS[(key0 + i) * 16 + l16] = dS[kt][i];
     }
-    if (c > c_lo) fetch(c - 1);
     __syncthreads();
+    if (c > c_lo) fetch(c - 1, 0);
     // dE = Bq^T dO + Kc dS for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -768,6 +794,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
       snE[r * 16 + l16] = -acc[i];
     }
     __syncthreads();
+    if (c > c_lo) fetch(c - 1, 1);
     // dS <- Diag(gamma) dS + Qg^T dO - W^T dE
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
