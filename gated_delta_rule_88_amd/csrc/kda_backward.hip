@@ -644,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
     if (c + 1 < c_hi) fetch(c + 1, 0);
     // E = U - W S for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
+#pragma unroll
     for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sW[(16 * w + l16) * LW + k0 + g], sS[(k0 + g) * 16 + l16], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void bwd_fwd(const int32_t* __restrict__ 
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt);
       S[kt] *= gam[kt];
-#pragma unroll 4
+#pragma unroll
       for (int t = 0; t < C; t += 4) S[kt] = mfma4(sKc[(t + g) * LK + key0 + l16], sE[(t + g) * 16 + l16], S[kt]);
     }
     __syncthreads();
@@ -783,9 +783,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
     if (c > c_lo) fetch(c - 1, 0);
     // dE = Bq^T dO + Kc dS for token tile w
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < C; s += 4) acc = mfma4(sBq[(s + g) * LC + 16 * w + l16], sdO[(s + g) * 16 + l16], acc);
 #pragma unroll 8
+    for (int s = 0; s < C; s += 4) acc = mfma4(sBq[(s + g) * LC + 16 * w + l16], sdO[(s + g) * 16 + l16], acc);
+#pragma unroll 16
     for (int k0 = 0; k0 < D; k0 += 4) acc = mfma4(sKc[(16 * w + l16) * LR + k0 + g], sdS[(k0 + g) * 16 + l16], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate(const int32_t* __restrict
     for (int kt = 0; kt < KTW; ++kt) {
       const int key0 = 16 * (w * KTW + kt);
       dS[kt] *= gam[kt];
-#pragma unroll 4
+#pragma unroll 8
       for (int t = 0; t < C; t += 4) {
         dS[kt] = mfma4(sQg[(t + g) * LK + key0 + l16], sdO[(t + g) * 16 + l16], dS[kt]);
         dS[kt] = mfma4(sW[(t + g) * LK + key0 + l16], snE[(t + g) * 16 + l16], dS[kt]);
