@@ -75,8 +75,8 @@ struct Ws {
   static constexpr int64_t KX = 0, QX = CD, VX = 2 * CD, DOX = 3 * CD, KA = 4 * CD, KB = 5 * CD, QA = 6 * CD,
                            KG = 7 * CD, QG = 8 * CD, KC = 9 * CD, EG = 10 * CD, EC = 11 * CD, EGA = 12 * CD,
                            EAG = 13 * CD, W = 14 * CD, U = 15 * CD, E = 16 * CD, DE = 17 * CD, DQ = 18 * CD,
-                           DKP = 19 * CD, DKC = 20 * CD, DW = 21 * CD, P = 22 * CD, R = 23 * CD, DKM = 24 * CD;
-  static constexpr int64_t A = 25 * CD, BQ = A + CC, T = BQ + CC, TB = T + CC, DBQ = TB + CC, DT = DBQ + CC,
+                           DKP = 19 * CD, DKM = 20 * CD, DW = 21 * CD;
+  static constexpr int64_t A = 22 * CD, BQ = A + CC, T = BQ + CC, TB = T + CC, DBQ = TB + CC, DT = DBQ + CC,
                            X = DT + CC, DA = X + CC, DMA = DA + CC;
   static constexpr int64_t DS = DMA + CC;
   static constexpr int64_t BETA = DS + DD, DBQD = BETA + C, GAM = DBQD + C;
@@ -264,6 +264,158 @@ __device__ __forceinline__ void wg_mm(const Mat A1, const Mat B1, int K1, const 
   }
 }
 
+// Two products with a shared right operand, out1 = A1 B and out2 = A2 B
+// (each 64 x N, K a multiple of 32), in the lane layout of wg_mm: B's panels
+// are loaded and staged once for both.  Uses kGemmLds2 floats of LDS.
+constexpr int kGemmLds2 = 2 * 32 * 80 + 32 * 144;
+
+template <int N>
+__device__ __forceinline__ void wg_mm2(const Mat A1, const Mat A2, const Mat B, int K, float* lds,
+                                       f32x4 (&acc1)[N / 16], f32x4 (&acc2)[N / 16]) {
+  constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
+  lfloat* sA1 = loc(lds);
+  lfloat* sA2 = loc(lds) + 32 * LA;
+  lfloat* sB = loc(lds) + 64 * LA;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt) acc1[nt] = acc2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ra1[2], ra2[2], rb[NBQ];
+  auto loadA = [&](const Mat& A, f32x4 (&ra)[2], int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      ra[it] = A.cs == 1 ? ld4(A.p + (int64_t)(idx & 63) * A.rs + k0 + 4 * (idx >> 6))
+                         : ld4(A.p + (int64_t)(k0 + (idx >> 4)) * A.cs + 4 * (idx & 15));
+    }
+  };
+  auto load = [&](int k0) {
+    loadA(A1, ra1, k0);
+    loadA(A2, ra2, k0);
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      rb[it] = B.cs == 1 ? ld4(B.p + (int64_t)(k0 + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                         : ld4(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
+    }
+  };
+  auto stageA = [&](const Mat& A, const f32x4 (&ra)[2], lfloat* sA) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      if (A.cs == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sA[(4 * (idx >> 6) + i) * LA + (idx & 63)] = ra[it][i];
+      } else {
+        *(lf32x4*)(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
+      }
+    }
+  };
+  __syncthreads();
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    stageA(A1, ra1, sA1);
+    stageA(A2, ra2, sA2);
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      if (B.cs == 1) {
+        *(lf32x4*)(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sB[(4 * (idx / N) + i) * LB + idx % N] = rb[it][i];
+      }
+    }
+    __syncthreads();
+    if (k0 + 32 < K) load(k0 + 32);
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      const float a1 = sA1[(kk + g) * LA + 16 * w + l16], a2 = sA2[(kk + g) * LA + 16 * w + l16];
+#pragma unroll
+      for (int nt = 0; nt < N / 16; ++nt) {
+        const float b = sB[(kk + g) * LB + 16 * nt + l16];
+        acc1[nt] = mfma4(a1, b, acc1[nt]);
+        acc2[nt] = mfma4(a2, b, acc2[nt]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Two products with a shared left operand, out1 = A B1 and out2 = A B2, the
+// counterpart of wg_mm2.  Uses kGemmLds3 floats of LDS.
+constexpr int kGemmLds3 = 32 * 80 + 2 * 32 * 144;
+
+template <int N>
+__device__ __forceinline__ void wg_mm2b(const Mat A, const Mat B1, const Mat B2, int K, float* lds,
+                                        f32x4 (&acc1)[N / 16], f32x4 (&acc2)[N / 16]) {
+  constexpr int LA = 80, LB = N + 16, NBQ = 8 * N / 256;
+  lfloat* sA = loc(lds);
+  lfloat* sB1 = loc(lds) + 32 * LA;
+  lfloat* sB2 = sB1 + 32 * LB;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, l16 = l & 15;
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt) acc1[nt] = acc2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ra[2], rb1[NBQ], rb2[NBQ];
+  auto loadB = [&](const Mat& B, f32x4 (&rb)[NBQ], int k0) {
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      rb[it] = B.cs == 1 ? ld4(B.p + (int64_t)(k0 + idx / (N / 4)) * B.rs + 4 * (idx % (N / 4)))
+                         : ld4(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
+    }
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      ra[it] = A.cs == 1 ? ld4(A.p + (int64_t)(idx & 63) * A.rs + k0 + 4 * (idx >> 6))
+                         : ld4(A.p + (int64_t)(k0 + (idx >> 4)) * A.cs + 4 * (idx & 15));
+    }
+    loadB(B1, rb1, k0);
+    loadB(B2, rb2, k0);
+  };
+  auto stageB = [&](const Mat& B, const f32x4 (&rb)[NBQ], lfloat* sB) {
+#pragma unroll
+    for (int it = 0; it < NBQ; ++it) {
+      const int idx = tid + 256 * it;
+      if (B.cs == 1) {
+        *(lf32x4*)(sB + (idx / (N / 4)) * LB + 4 * (idx % (N / 4))) = rb[it];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sB[(4 * (idx / N) + i) * LB + idx % N] = rb[it][i];
+      }
+    }
+  };
+  __syncthreads();
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      if (A.cs == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sA[(4 * (idx >> 6) + i) * LA + (idx & 63)] = ra[it][i];
+      } else {
+        *(lf32x4*)(sA + (idx >> 4) * LA + 4 * (idx & 15)) = ra[it];
+      }
+    }
+    stageB(B1, rb1, sB1);
+    stageB(B2, rb2, sB2);
+    __syncthreads();
+    if (k0 + 32 < K) load(k0 + 32);
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 4) {
+      const float a = sA[(kk + g) * LA + 16 * w + l16];
+#pragma unroll
+      for (int nt = 0; nt < N / 16; ++nt) {
+        acc1[nt] = mfma4(a, sB1[(kk + g) * LB + 16 * nt + l16], acc1[nt]);
+        acc2[nt] = mfma4(a, sB2[(kk + g) * LB + 16 * nt + l16], acc2[nt]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 constexpr Mat kNoMat = {nullptr, 1, 1};
 
 // What the epilogue of a 64 x D product does with acc, the product (every
@@ -272,6 +424,11 @@ constexpr Mat kNoMat = {nullptr, 1, 1};
 //   store = acc * store_scale;  out[(row) * out_rs + col] = beta_row * acc
 //   for rows < len (the value gradient, straight into the output);
 //   x  = (x_add ? x : 0) + s_row * acc * fx
+//   rowsum[row] = sum over columns of acc * rf        (fp32, LDS [C])
+//   colsum[(4 w + g) * D + col] = sum over the lane's four rows of acc * cf
+//                                 (fp64, LDS [16][D]: one partial per
+//                                 (wave, lane group); their sum is the
+//                                 column sum)
 // with s_row = beta_row when row_beta, else 1.  Each part loads everything
 // it needs (half a tile at a time) before its first store, so a lane keeps
 // its loads in flight.
@@ -286,14 +443,15 @@ struct EpiD {
   bool x_add = false;
   bool row_beta = false;
   const float* beta = nullptr;
+  float* rowsum = nullptr;
+  const float* rf = nullptr;
+  double* colsum = nullptr;
+  const float* cf = nullptr;
 };
 
 template <int D>
-__device__ __attribute__((noinline)) void gemm_d(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2,
-                                                 int K2, float* lds, const EpiD e) {
+__device__ __forceinline__ void epilogue_d(const f32x4 (&acc)[D / 16], const EpiD& e) {
   constexpr int NT = D / 16;
-  f32x4 acc[NT];
-  wg_mm<D>(A1, B1, K1, A2, B2, K2, lds, acc);
   const int tid = threadIdx.x, w = tid >> 6, g = (tid & 63) >> 4, l16 = tid & 15;
   const int64_t lane = (int64_t)(16 * w + 4 * g) * D + l16;   // this lane's first element
   gcfloat* beta = glb(e.beta);
@@ -339,6 +497,75 @@ __device__ __attribute__((noinline)) void gemm_d(const Mat A1, const Mat B1, int
           x[lane + i * D + 16 * (n0 + nt)] = xv[nt][i] + s[i] * acc[n0 + nt][i] * f[nt][i];
     }
   }
+  if (e.rowsum) {
+    gcfloat* rf = glb(e.rf);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n0 = 0; n0 < NT; n0 += NH) {
+      f32x4 f[NH];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[nt][i] = rf[lane + i * D + 16 * (n0 + nt)];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] += acc[n0 + nt][i] * f[nt][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // across the 16 lanes that hold the row
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) part[i] += __shfl_xor(part[i], m);
+      if (l16 == 0) loc(e.rowsum)[16 * w + 4 * g + i] = part[i];
+    }
+  }
+  if (e.colsum) {
+    gcfloat* cf = glb(e.cf);
+    __attribute__((address_space(3))) double* cs = (__attribute__((address_space(3))) double*)e.colsum;
+#pragma unroll
+    for (int n0 = 0; n0 < NT; n0 += NH) {
+      f32x4 f[NH];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[nt][i] = cf[lane + i * D + 16 * (n0 + nt)];
+#pragma unroll
+      for (int nt = 0; nt < NH; ++nt) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t += (double)acc[n0 + nt][i] * (double)f[nt][i];
+        cs[(4 * w + g) * D + 16 * (n0 + nt) + l16] = t;
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2,
+                                                 int K2, float* lds, const EpiD e) {
+  f32x4 acc[D / 16];
+  wg_mm<D>(A1, B1, K1, A2, B2, K2, lds, acc);
+  epilogue_d<D>(acc, e);
+}
+
+// out1 = A1 B and out2 = A2 B, each with its own epilogue.
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d2(const Mat A1, const Mat A2, const Mat B, int K, float* lds,
+                                                  const EpiD e1, const EpiD e2) {
+  f32x4 acc1[D / 16], acc2[D / 16];
+  wg_mm2<D>(A1, A2, B, K, lds, acc1, acc2);
+  epilogue_d<D>(acc1, e1);
+  epilogue_d<D>(acc2, e2);
+}
+
+// out1 = A B1 and out2 = A B2, each with its own epilogue.
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d2b(const Mat A, const Mat B1, const Mat B2, int K, float* lds,
+                                                   const EpiD e1, const EpiD e2) {
+  f32x4 acc1[D / 16], acc2[D / 16];
+  wg_mm2b<D>(A, B1, B2, K, lds, acc1, acc2);
+  epilogue_d<D>(acc1, e1);
+  epilogue_d<D>(acc2, e2);
 }
 
 template <class In>
@@ -827,7 +1054,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
                                                      float* __restrict__ gk, float* __restrict__ gv,
                                                      float* __restrict__ gla, float* __restrict__ gbeta) {
   using L = Ws<D>;
-  __shared__ __align__(16) float lds[kGemmLds];
+  __shared__ __align__(16) float lds[kGemmLds3 > kGemmLds2 ? kGemmLds3 : kGemmLds2];
+  __shared__ float sPV[C], sRK[C];    // rowsum(P o V), rowsum(R o Kg)
+  __shared__ double sKc[16 * D];      // partial colsums of dKc o Kc
   const int64_t item = blockIdx.x, slot = win.slot_lo + item / H;
   const int h = (int)(item % H);
   int n, len;
@@ -847,39 +1076,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     glb(B)[L::DBQ + r * C + s] = s < r ? x : 0.f;
     if (s == r) glb(B)[L::DBQD + r] = x;
   });
-  {  // dQg = dO S0^T: dQ = dQg e^G
-    EpiD e;
-    e.x = F(L::DQ); e.fx = F(L::EG);
-    gemm_d<D>(M(L::DOX, D, 1), Mat{S0, D, 1}, D, kNoMat, kNoMat, 0, lds, e);
+  {  // dQg = dO S0^T: dQ = dQg e^G; dW = -dE S0^T
+    EpiD e1, e2;
+    e1.x = F(L::DQ); e1.fx = F(L::EG);
+    e2.store = F(L::DW); e2.store_scale = -1.f;
+    gemm_d2<D>(M(L::DOX, D, 1), M(L::DE, D, 1), Mat{S0, D, 1}, D, lds, e1, e2);
   }
-  {  // dQa = dBs Kb: dQ += dQa e^(G-a)
+  {  // dKc = E dS_end^T: dKm = dKc e^(gC-G); colsum(dKc o Kc) for dgC
     EpiD e;
-    e.x = F(L::DQ); e.fx = F(L::EGA); e.x_add = true;
-    gemm_d<D>(M(L::DBQ, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
-  }
-  {  // dKc = E dS_end^T: dKm = dKc e^(gC-G)
-    EpiD e;
-    e.store = F(L::DKC);
     e.x = F(L::DKM); e.fx = F(L::EC);
+    e.colsum = sKc; e.cf = F(L::KC);
     gemm_d<D>(M(L::E, D, 1), M(L::DS, D, 1), D, kNoMat, kNoMat, 0, lds, e);
   }
-  {  // dW = -dE S0^T
-    EpiD e;
-    e.store = F(L::DW); e.store_scale = -1.f;
-    gemm_d<D>(M(L::DE, D, 1), Mat{S0, D, 1}, D, kNoMat, kNoMat, 0, lds, e);
-  }
-  {  // P = T^T dE: dV = Diag(beta) P
-    EpiD e;
-    e.store = F(L::P);
-    e.out = gv + (t0 * H + h) * D; e.out_rs = (int64_t)H * D; e.len = len; e.beta = beta;
-    gemm_d<D>(M(L::T, 1, C), M(L::DE, D, 1), C, kNoMat, kNoMat, 0, lds, e);
-  }
-  {  // R = T^T dW: dKg = Diag(beta) R: dKp = dKg e^G
-    EpiD e;
-    e.store = F(L::R);
-    e.x = F(L::DKP); e.fx = F(L::EG);
-    e.row_beta = true; e.beta = beta;
-    gemm_d<D>(M(L::T, 1, C), M(L::DW, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  {  // P = T^T dE: dV = Diag(beta) P; rowsum(P o V) for dbeta;
+     // R = T^T dW: dKg = Diag(beta) R: dKp = dKg e^G; rowsum(R o Kg) for dbeta
+    EpiD e1, e2;
+    e1.out = gv + (t0 * H + h) * D; e1.out_rs = (int64_t)H * D; e1.len = len; e1.beta = beta;
+    e1.rowsum = sPV; e1.rf = F(L::VX);
+    e2.x = F(L::DKP); e2.fx = F(L::EG);
+    e2.rowsum = sRK; e2.rf = F(L::KG);
+    e2.row_beta = true; e2.beta = beta;
+    gemm_d2b<D>(M(L::T, 1, C), M(L::DE, D, 1), M(L::DW, D, 1), C, lds, e1, e2);
   }
   // dT = dE (Diag(beta) V)^T + dW (Diag(beta) Kg)^T  (beta of the column)
   {
@@ -900,10 +1117,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     glb(B)[L::DA + r * C + s] = s < r ? glb(beta)[r] * dm : 0.f;
     glb(B)[L::DMA + r * C + s] = s < r ? dm * glb(B)[L::A + r * C + s] : 0.f;
   });
-  {  // dKa = dA Kb: dKp += dKa e^(G-a)
-    EpiD e;
-    e.x = F(L::DKP); e.fx = F(L::EGA); e.x_add = true;
-    gemm_d<D>(M(L::DA, C, 1), M(L::KB, D, 1), C, kNoMat, kNoMat, 0, lds, e);
+  {  // dQa = dBs Kb: dQ += dQa e^(G-a); dKa = dA Kb: dKp += dKa e^(G-a)
+    EpiD e1, e2;
+    e1.x = F(L::DQ); e1.fx = F(L::EGA); e1.x_add = true;
+    e2.x = F(L::DKP); e2.fx = F(L::EGA); e2.x_add = true;
+    gemm_d2<D>(M(L::DBQ, C, 1), M(L::DA, C, 1), M(L::KB, D, 1), C, lds, e1, e2);
   }
   {  // dKb = dA^T Ka + dBs^T Qa: dKm += dKb e^(a-G)
     EpiD e;
@@ -924,8 +1142,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
 #pragma unroll 16
     for (int j = grp * JG; j < (grp + 1) * JG; ++j)
       dgam += (double)B[L::DS + (int64_t)j * D + c] * (double)S0[(int64_t)j * D + c];
-#pragma unroll 16
-    for (int r = grp * RG; r < (grp + 1) * RG; ++r) dkc += (double)at(L::DKC, r, c) * (double)at(L::KC, r, c);
+    for (int x = grp * (16 / NG); x < (grp + 1) * (16 / NG); ++x) dkc += sKc[x * D + c];
     // partial of dgC = rowsum(dS_end o S0) gamma + colsum(dKc o Kc)
     sRed[grp * D + c] = dgam * (double)B[L::GAM + c] + dkc;
   }
@@ -968,17 +1185,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
       }
     }
   }
-  // dbeta: wave w reduces rows [16 w, 16 w + 16), its lanes across columns
+  // dbeta = rowsum(P o V) + rowsum(R o Kg) + rowsum(strict_lower(dM) o A):
+  // wave w reduces the last term over rows [16 w, 16 w + 16), its lanes
+  // across columns
 #pragma unroll 4
   for (int rr = 0; rr < 16; ++rr) {
-    const int r = 16 * w + rr;
-    float part = 0.f;
-#pragma unroll
-    for (int j = l; j < D; j += 64) part += at(L::P, r, j) * at(L::VX, r, j) + at(L::R, r, j) * at(L::KG, r, j);
-    part += B[L::DMA + r * C + l];   // strictly lower: zero for l >= r
+    const int r = 16 * (tid >> 6) + rr;
+    float part = B[L::DMA + r * C + l];   // strictly lower: zero for l >= r
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-    if (l == 0 && r < len) gbeta[(t0 + r) * H + h] = part;
+    if (l == 0 && r < len) gbeta[(t0 + r) * H + h] = sPV[r] + sRK[r] + part;
   }
 }
 

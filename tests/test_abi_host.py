@@ -158,11 +158,11 @@ def test_decode_pooled_zero_sequences_is_a_no_op(lib):
 
 def test_backward_workspace_size(lib):
     f = lib.kda_prefill_backward_workspace_size
-    # a window of per-(chunk slot, head) blocks -- 25 fp32 [64 x d] matrices, 9
+    # a window of per-(chunk slot, head) blocks -- 22 fp32 [64 x d] matrices, 9
     # fp32 [64 x 64], the dS_end block [d x d] and the beta, diag(dBq), e^gC
     # vectors -- of at most 512 slots and 8 GiB; then the state entering every
     # chunk slot [d x d] and one [d x d] carry per (sequence, head)
-    block_128 = 4 * (25 * 64 * 128 + 9 * 64 * 64 + 128 * 128 + 2 * 64 + 128)
+    block_128 = 4 * (22 * 64 * 128 + 9 * 64 * 64 + 128 * 128 + 2 * 64 + 128)
     state = 4 * 128 * 128
 
     def expect(n, t, h):
