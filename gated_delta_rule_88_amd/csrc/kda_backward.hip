@@ -558,6 +558,80 @@ __device__ __attribute__((noinline)) void gemm_d2(const Mat A1, const Mat A2, co
   epilogue_d<D>(acc2, e2);
 }
 
+// out1 = A1 B and out2 = A2 B added to two sums with the same factor:
+// x1 += p1 fx and x2 += p2 fx (no row scale), fx loaded once.
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d2_addf(const Mat A1, const Mat A2, const Mat B, int K, float* lds,
+                                                       float* x1, float* x2, const float* fx) {
+  constexpr int NT = D / 16, NH = NT > 4 ? NT / 2 : NT;
+  f32x4 acc1[NT], acc2[NT];
+  wg_mm2<D>(A1, A2, B, K, lds, acc1, acc2);
+  const int tid = threadIdx.x, w = tid >> 6, g = (tid & 63) >> 4, l16 = tid & 15;
+  const int64_t lane = (int64_t)(16 * w + 4 * g) * D + l16;
+  gcfloat* f = glb(fx);
+  gfloat* y1 = glb(x1);
+  gfloat* y2 = glb(x2);
+#pragma unroll
+  for (int n0 = 0; n0 < NT; n0 += NH) {
+    f32x4 fv[NH], v1[NH], v2[NH];
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t o = lane + i * D + 16 * (n0 + nt);
+        fv[nt][i] = f[o];
+        v1[nt][i] = y1[o];
+        v2[nt][i] = y2[o];
+      }
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t o = lane + i * D + 16 * (n0 + nt);
+        y1[o] = v1[nt][i] + acc1[n0 + nt][i] * fv[nt][i];
+        y2[o] = v2[nt][i] + acc2[n0 + nt][i] * fv[nt][i];
+      }
+  }
+}
+
+// x = p1 fx1 + p2 fx2 for two products p1 = A1 B1 (K1) and p2 = A2 B2 +
+// A3 B3 (K2 each) computed one after the other, x written once (no
+// read-modify-write); e1 also carries p1's other epilogue parts (e1.x and
+// e1.fx are x and fx1).
+template <int D>
+__device__ __attribute__((noinline)) void gemm_d_sum2(const Mat A1, const Mat B1, int K1, const Mat A2, const Mat B2,
+                                                      const Mat A3, const Mat B3, int K2, const float* fx2,
+                                                      float* lds, const EpiD e1) {
+  constexpr int NT = D / 16, NH = NT > 4 ? NT / 2 : NT;
+  f32x4 acc1[NT], acc2[NT];
+  wg_mm<D>(A1, B1, K1, kNoMat, kNoMat, 0, lds, acc1);
+  EpiD e = e1;
+  e.x = nullptr;
+  epilogue_d<D>(acc1, e);
+  wg_mm<D>(A2, B2, K2, A3, B3, K2, lds, acc2);
+  const int tid = threadIdx.x, w = tid >> 6, g = (tid & 63) >> 4, l16 = tid & 15;
+  const int64_t lane = (int64_t)(16 * w + 4 * g) * D + l16;
+  gcfloat* f1 = glb(e1.fx);
+  gcfloat* f2 = glb(fx2);
+  gfloat* x = glb(e1.x);
+#pragma unroll
+  for (int n0 = 0; n0 < NT; n0 += NH) {
+    f32x4 a[NH], b[NH];
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[nt][i] = f1[lane + i * D + 16 * (n0 + nt)];
+        b[nt][i] = f2[lane + i * D + 16 * (n0 + nt)];
+      }
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[lane + i * D + 16 * (n0 + nt)] = (0.f + acc1[n0 + nt][i] * a[nt][i]) + acc2[n0 + nt][i] * b[nt][i];
+  }
+}
+
 // out1 = A B1 and out2 = A B2, each with its own epilogue.
 template <int D>
 __device__ __attribute__((noinline)) void gemm_d2b(const Mat A, const Mat B1, const Mat B2, int K, float* lds,
@@ -1082,12 +1156,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     e2.store = F(L::DW); e2.store_scale = -1.f;
     gemm_d2<D>(M(L::DOX, D, 1), M(L::DE, D, 1), Mat{S0, D, 1}, D, lds, e1, e2);
   }
-  {  // dKc = E dS_end^T: dKm = dKc e^(gC-G); colsum(dKc o Kc) for dgC
-    EpiD e;
-    e.x = F(L::DKM); e.fx = F(L::EC);
-    e.colsum = sKc; e.cf = F(L::KC);
-    gemm_d<D>(M(L::E, D, 1), M(L::DS, D, 1), D, kNoMat, kNoMat, 0, lds, e);
-  }
   {  // P = T^T dE: dV = Diag(beta) P; rowsum(P o V) for dbeta;
      // R = T^T dW: dKg = Diag(beta) R: dKp = dKg e^G; rowsum(R o Kg) for dbeta
     EpiD e1, e2;
@@ -1117,16 +1185,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_grad(const int32_t* __restric
     glb(B)[L::DA + r * C + s] = s < r ? glb(beta)[r] * dm : 0.f;
     glb(B)[L::DMA + r * C + s] = s < r ? dm * glb(B)[L::A + r * C + s] : 0.f;
   });
-  {  // dQa = dBs Kb: dQ += dQa e^(G-a); dKa = dA Kb: dKp += dKa e^(G-a)
-    EpiD e1, e2;
-    e1.x = F(L::DQ); e1.fx = F(L::EGA); e1.x_add = true;
-    e2.x = F(L::DKP); e2.fx = F(L::EGA); e2.x_add = true;
-    gemm_d2<D>(M(L::DBQ, C, 1), M(L::DA, C, 1), M(L::KB, D, 1), C, lds, e1, e2);
-  }
-  {  // dKb = dA^T Ka + dBs^T Qa: dKm += dKb e^(a-G)
+  // dQa = dBs Kb: dQ += dQa e^(G-a); dKa = dA Kb: dKp += dKa e^(G-a)
+  gemm_d2_addf<D>(M(L::DBQ, C, 1), M(L::DA, C, 1), M(L::KB, D, 1), C, lds, F(L::DQ), F(L::DKP), F(L::EGA));
+  {  // dKc = E dS_end^T, colsum(dKc o Kc) for dgC; dKb = dA^T Ka + dBs^T Qa;
+     // dKm = dKc e^(gC-G) + dKb e^(a-G)
     EpiD e;
-    e.x = F(L::DKM); e.fx = F(L::EAG); e.x_add = true;
-    gemm_d<D>(M(L::DA, 1, C), M(L::KA, D, 1), C, M(L::DBQ, 1, C), M(L::QA, D, 1), C, lds, e);
+    e.x = F(L::DKM); e.fx = F(L::EC);
+    e.colsum = sKc; e.cf = F(L::KC);
+    gemm_d_sum2<D>(M(L::E, D, 1), M(L::DS, D, 1), D, M(L::DA, 1, C), M(L::KA, D, 1), M(L::DBQ, 1, C),
+                   M(L::QA, D, 1), C, F(L::EAG), lds, e);
   }
   __syncthreads();
 
