@@ -313,10 +313,10 @@ kda_status kda_decode_step_pooled(const void* q, const void* k, const void* v,
  *                    the state entering every 64-token chunk (64 KiB per
  *                    (chunk, head) at dk = 128), one dL/dS per (sequence,
  *                    head), and the full factors of a window of at most 512
- *                    chunk slots and 8 GiB (1.07 MB per (chunk, head)); longer
+ *                    chunk slots and 8 GiB (0.93 MB per (chunk, head)); longer
  *                    calls run window by window, recomputing each window's
  *                    factors once more (17.5 GB for 16 sequences of 270,810
- *                    tokens at 32 heads, 25.8 GB for 2^20 tokens at 16).
+ *                    tokens at 32 heads, 24.8 GB for 2^20 tokens at 16).
  * Gradients are fp32 whatever `dtype` is.  Zero-length sequences give
  * grad_init_state = grad_final_state.  Errors as for kda_prefill_varlen.
  */
