@@ -135,10 +135,11 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
   f32x4 acc[N / 16];
 #pragma unroll
   for (int nt = 0; nt < N / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // one 32-deep panel of A and B in registers: loaded one panel ahead, so
-  // the next panel's loads are in flight while this one is multiplied
-  f32x4 ra[2], rb[NBQ];
-  auto load = [&](int k0) {
+  // 32-deep panels of A and B in registers, two sets in turn: each panel is
+  // loaded two panels ahead, so the loads of the next two are in flight
+  // while one is multiplied
+  f32x4 ra0[2], rb0[NBQ], ra1[2], rb1[NBQ];
+  auto load = [&](int k0, f32x4 (&ra)[2], f32x4 (&rb)[NBQ]) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int idx = tid + 256 * it;
@@ -152,9 +153,7 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
                          : ld4(B.p + (int64_t)(idx % N) * B.cs + k0 + 4 * (idx / N));
     }
   };
-  __syncthreads();   // operands written just before by other threads are visible
-  load(0);
-  for (int k0 = 0; k0 < Kd; k0 += 32) {
+  auto panel = [&](int k0, f32x4 (&ra)[2], f32x4 (&rb)[NBQ]) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int idx = tid + 256 * it;
@@ -178,7 +177,7 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
       }
     }
     __syncthreads();
-    if (k0 + 32 < Kd) load(k0 + 32);
+    if (k0 + 64 < Kd) load(k0 + 64, ra, rb);
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 4) {
       const float a = sA[(kk + g) * LA + 16 * w + l16];
@@ -186,6 +185,13 @@ __device__ __attribute__((noinline)) void wg_gemm(const Mat A, const Mat B, int 
       for (int nt = 0; nt < N / 16; ++nt) acc[nt] = mfma4(a, sB[(kk + g) * LB + 16 * nt + l16], acc[nt]);
     }
     __syncthreads();
+  };
+  __syncthreads();   // operands written just before by other threads are visible
+  load(0, ra0, rb0);
+  if (32 < Kd) load(32, ra1, rb1);
+  for (int k0 = 0; k0 < Kd; k0 += 64) {
+    panel(k0, ra0, rb0);
+    if (k0 + 32 < Kd) panel(k0 + 32, ra1, rb1);
   }
 #pragma unroll
   for (int nt = 0; nt < N / 16; ++nt)
