@@ -89,9 +89,16 @@ struct Rec {
   static constexpr size_t KC = QP + 4 * KB * FB;             // [NT key tiles][2]            Kc^T
   static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f16x4
   static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 8;  // same tiles of (Bqk U)^T: token l%16, columns 4 (l/16) + e
+  // (the records of the read-out O = Qg S + Bqk E hold Qg in place of Q' and,
+  // in place of (Bqk U)^T, the A fragments of Bqk over tokens: token tile w,
+  // token blocks pb <= w / 2, at bq_frag(w, pb))
   static constexpr size_t G = BU + (size_t)NT * 4 * 64 * 8;  // [D] fp32 e^G[C-1]
   static constexpr size_t BYTES = G + (size_t)D * 4;
 };
+
+// Fragment index of Bqk (token tile w, token block pb <= w / 2) in the BU
+// region of a record of the Qg / Bqk read-out: six fragments of 1 KiB.
+__device__ __forceinline__ int bq_frag(int w, int pb) { return (w < 2 ? w : 2 * w - 2) + pb; }
 
 // LDS plan of the prep workgroup (bytes; two workgroups fit one CU).
 //   region X: Kbar fragments of one stage of key blocks and the Kc^T
@@ -147,8 +154,11 @@ __device__ __forceinline__ float row_shr(float v) {   // lane i of a DPP row get
 // ---------------------------------------------------------------------------
 // SCALAR: one gate per (token, head) instead of one per key channel; RAW: q,
 // k unnormalised and beta a logit (normalised in the kernel).  Both are
-// compile-time so that the input loads carry no branch.
-template <int D, bool SCALAR, bool RAW>
+// compile-time so that the input loads carry no branch.  QGB: the record
+// carries Qg and Bqk for the read-out O = Qg S + Bqk E instead of Q' and
+// (Bqk U)^T: no phase G, and 6 KiB of Bqk written in place of 16 KiB of
+// (Bqk U)^T.
+template <int D, bool SCALAR, bool RAW, bool QGB>
 __device__ __forceinline__ void prep_item(
     const In* __restrict__ q, const In* __restrict__ k, const In* __restrict__ v,
     const float* __restrict__ log_alpha, const In* __restrict__ beta, int H, int h, int64_t t0, int len,
@@ -367,6 +377,7 @@ __device__ __forceinline__ void prep_item(
   // Bqk as the A operand over tokens (rows: this wave's tokens), split; the
   // Bqk^T tiles (j, w) are, lane for lane, its fragments
   Frag bqH[2], bqL[2];
+  HFrag bqF[2];   // single fp16, for a Qg / Bqk record
 #pragma unroll
   for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
@@ -378,8 +389,21 @@ __device__ __forceinline__ void prep_item(
         const In hv = (In)x;
         bqH[pb][4 * hf + e] = hv;
         bqL[pb][4 * hf + e] = (In)(x - (float)hv);
+        bqF[pb][4 * hf + e] = (_Float16)x;
       }
     }
+  if constexpr (QGB) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+      if (pb <= (w >> 1)) st_rec<HFrag>(rs, R::BU + ((size_t)bq_frag(w, pb) * 64 + l) * 16, bqF[pb]);
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      HFrag qh;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) qh[m] = (_Float16)qg[p][m];
+      st_rec<HFrag>(rs, R::QP + ((w * KB + p) * 64 + l) * 16, qh);
+    }
+  }
   __syncthreads();   // region X is reused for L and T
 
   // ---- D: T = (I + L)^-1, L = Diag(beta) A strictly lower ---------------------
@@ -502,10 +526,13 @@ __device__ __forceinline__ void prep_item(
   __syncthreads();   // Kg^T and T are no longer read
 
   // ---- F: -W tiles to LDS (A operand of W^T over tokens); U = T' V -> record,
-  //      and U split to LDS (B operand over tokens) --------------------------------
+  //      and U split to LDS (B operand over tokens); a Qg / Bqk record needs
+  //      only U -----------------------------------------------------------------
+  if constexpr (!QGB) {
 #pragma unroll
-  for (int it = 0; it < NT; ++it)
-    *reinterpret_cast<Half*>(lds + L::KGT + ((it * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1)) = wneg[it];
+    for (int it = 0; it < NT; ++it)
+      *reinterpret_cast<Half*>(lds + L::KGT + ((it * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1)) = wneg[it];
+  }
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
     f32x4 uc = {0.f, 0.f, 0.f, 0.f};
@@ -518,16 +545,19 @@ __device__ __forceinline__ void prep_item(
 #pragma unroll
     for (int e = 0; e < 4; ++e) u16[e] = (_Float16)uc[e];
     st_rec<HHalf>(rs, R::U + ((ct * 4 + w) * 64 + l) * 8, u16);
-    Half uh, ul;
+    if constexpr (!QGB) {
+      Half uh, ul;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uh[e] = (In)uc[e];
-      ul[e] = (In)(uc[e] - (float)uh[e]);
+      for (int e = 0; e < 4; ++e) {
+        uh[e] = (In)uc[e];
+        ul[e] = (In)(uc[e] - (float)uh[e]);
+      }
+      const size_t off = ((ct * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1);
+      *reinterpret_cast<Half*>(lds + L::UX + off) = uh;
+      *reinterpret_cast<Half*>(lds + L::UX + NT * 2 * FB + off) = ul;
     }
-    const size_t off = ((ct * 2 + (w >> 1)) * 64 + l) * 16 + 8 * (w & 1);
-    *reinterpret_cast<Half*>(lds + L::UX + off) = uh;
-    *reinterpret_cast<Half*>(lds + L::UX + NT * 2 * FB + off) = ul;
   }
+  if constexpr (QGB) return;
   __syncthreads();
 
   // ---- G: Q'^T = Qg^T - W^T Bqk^T (tiles (it, w)) -> record Q';
@@ -584,8 +614,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
   int n, len;
   int64_t t0;
   if (!decode_slot(cu, N, slot, n, t0, len)) return;   // whole workgroup: unused slot
-  prep_item<D, SCALAR, RAW>(q, k, v, log_alpha, beta, H, h, t0, len, ws + ((size_t)slot * H + h) * Rec<D>::BYTES,
-                            lds, status);
+  prep_item<D, SCALAR, RAW, false>(q, k, v, log_alpha, beta, H, h, t0, len,
+                                   ws + ((size_t)slot * H + h) * Rec<D>::BYTES, lds, status);
 }
 
 // ---------------------------------------------------------------------------
@@ -596,29 +626,40 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 // W, Q' and Kc serve every value tile of the slice, so a wider slice loads
 // them once for more columns.
 // ---------------------------------------------------------------------------
-template <int D, int VT>
+template <int D, int VT, bool QGB>
 struct Ops {
   static constexpr int KB = D / 32, KTW = D / 64;
-  HFrag w[KB];           // W, token tile of this wave
-  HFrag qp[KB];          // Q', token tile of this wave
-  HFrag kc[KTW][2];      // Kc^T for this wave's key tiles
-  HHalf u[VT], bu[VT];   // U and Bqk U, token tile of this wave, the slice's value tiles
-  f32x4 gam[KTW];        // e^G[C-1] for this lane's key rows
+  HFrag w[KB];               // W, token tile of this wave
+  HFrag qp[KB];              // Q' (or Qg), token tile of this wave
+  HFrag kc[KTW][2];          // Kc^T for this wave's key tiles
+  HHalf u[VT];               // U, token tile of this wave, the slice's value tiles
+  HHalf bu[QGB ? 1 : VT];    // (Bqk U)^T, same tiles
+  HFrag bq[QGB ? 2 : 1];     // Bqk over tokens, two token blocks (tiles 0, 1: the second is zero)
+  f32x4 gam[KTW];            // e^G[C-1] for this lane's key rows
 };
 
 // The operand loads of one chunk, in three parts that the step spreads over
 // its phases so that the vector memory path works while the MFMAs do.
-template <int D, int VT>
-__device__ __forceinline__ void load_ops_part(Ops<D, VT>& o, Rsrc rs, int part, int w, int l, int g, int vt0) {
+template <int D, int VT, bool QGB>
+__device__ __forceinline__ void load_ops_part(Ops<D, VT, QGB>& o, Rsrc rs, int part, int w, int l, int g, int vt0) {
   using R = Rec<D>;
-  using O = Ops<D, VT>;
+  using O = Ops<D, VT, QGB>;
   if (part == 0) {
 #pragma unroll
     for (int p = 0; p < O::KB; ++p) o.w[p] = ld_rec<HFrag>(rs, R::W + ((w * O::KB + p) * 64 + l) * 16);
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       o.u[t] = ld_rec<HHalf>(rs, R::U + (((vt0 + t) * 4 + w) * 64 + l) * 8);
-      o.bu[t] = ld_rec<HHalf>(rs, R::BU + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+      if constexpr (!QGB) o.bu[t] = ld_rec<HHalf>(rs, R::BU + (((vt0 + t) * 4 + w) * 64 + l) * 8);
+    }
+    if constexpr (QGB) {
+      // waves 0 and 1 have one block: their second fragment is zero, so
+      // that the read-out's products take no branch (a product under a
+      // lane mask would still run on every lane)
+      o.bq[0] = ld_rec<HFrag>(rs, R::BU + ((size_t)bq_frag(w, 0) * 64 + l) * 16);
+      const HFrag b1 = ld_rec<HFrag>(rs, R::BU + ((size_t)bq_frag(w, w >> 1) * 64 + l) * 16);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o.bq[1][m] = w >= 2 ? b1[m] : (_Float16)0.f;
     }
   } else if (part == 1) {
 #pragma unroll
@@ -637,10 +678,10 @@ __device__ __forceinline__ void load_ops_part(Ops<D, VT>& o, Rsrc rs, int part, 
   }
 }
 
-template <int D, int VT>
-__device__ __forceinline__ void load_ops(Ops<D, VT>& o, Rsrc rs, int w, int l, int g, int vt0) {
+template <int D, int VT, bool QGB>
+__device__ __forceinline__ void load_ops(Ops<D, VT, QGB>& o, Rsrc rs, int w, int l, int g, int vt0) {
 #pragma unroll
-  for (int part = 0; part < 3; ++part) load_ops_part<D, VT>(o, rs, part, w, l, g, vt0);
+  for (int part = 0; part < 3; ++part) load_ops_part<D, VT, QGB>(o, rs, part, w, l, g, vt0);
 }
 
 // Chunk-ready flags of the one-launch path: flag[slot * H + h] turns nonzero
@@ -707,7 +748,7 @@ struct StateLds {
 // HOLD_SF keeps this step's S fragments in registers for both products;
 // otherwise the read-out reads them from LDS again, from a copy that the
 // next step does not overwrite.  Both give the same results bit for bit.
-template <int D, int VT, int NB, bool HOLD_SF>
+template <int D, int VT, int NB, bool HOLD_SF, bool QGB>
 __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H, const float* init, float* fin,
                                            In* __restrict__ o, const unsigned char* __restrict__ ws,
                                            const int32_t* __restrict__ sidx, int pool_slots, int n, int h, int vt,
@@ -756,9 +797,9 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
   // chunk (record `nrs`) are loaded into `nxt`, one part per phase, once
   // the records up to chunk `need` are known to be published (need < 0:
   // an earlier step made sure of it)
-  auto step = [&](const Ops<D, VT>& ops, int c, Ops<D, VT>& nxt, Rsrc nrs, int need) {
+  auto step = [&](const Ops<D, VT, QGB>& ops, int c, Ops<D, VT, QGB>& nxt, Rsrc nrs, int need) {
     if (need >= 0) need_record(sy, slot0, H, h, need, nch, l, upto, failed);
-    load_ops_part<D, VT>(nxt, nrs, 0, w, l, g, vt0);
+    load_ops_part<D, VT, QGB>(nxt, nrs, 0, w, l, g, vt0);
     const int64_t t0 = bos + (int64_t)c * kChunk;
     const int len = (int)min<int64_t>(kChunk, eos - t0);
     HFrag (*sSc)[KB][64] = sS(c);
@@ -773,7 +814,7 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
         *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sSc[t][kti >> 1][l]) + 4 * (kti & 1)) = hs;
       }
     __syncthreads();
-    load_ops_part<D, VT>(nxt, nrs, 1, w, l, g, vt0);
+    load_ops_part<D, VT, QGB>(nxt, nrs, 1, w, l, g, vt0);
     // token tile w: W S first -- E gates the other waves; Q' S only after
     // the state update has been issued
     HFrag sf[HOLD_SF ? VT : 1][KB];
@@ -795,7 +836,7 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
       *reinterpret_cast<HHalf*>(reinterpret_cast<_Float16*>(&sE[t][w >> 1][l]) + 4 * (w & 1)) = eh;
     }
     __syncthreads();
-    load_ops_part<D, VT>(nxt, nrs, 2, w, l, g, vt0);
+    load_ops_part<D, VT, QGB>(nxt, nrs, 2, w, l, g, vt0);
     // S <- Diag(e^G[C-1]) S + Kc^T E
 #pragma unroll
     for (int t = 0; t < VT; ++t)
@@ -813,8 +854,15 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       f32x4 ot;
+      if constexpr (QGB) {
+        // O^T = S^T Qg^T + E^T Bqk^T: E of this chunk is still in LDS
+        ot = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ot[e] = (float)ops.bu[t][e];
+        for (int pb = 0; pb < 2; ++pb) mma(ot, sE[t][pb][l], ops.bq[pb]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[e] = (float)ops.bu[t][e];
+      }
 #pragma unroll
       for (int p = 0; p < KB; ++p) mma(ot, HOLD_SF ? sf[HOLD_SF ? t : 0][p] : sSc[t][p][l], ops.qp[p]);
       Half ob;
@@ -838,13 +886,13 @@ __device__ __forceinline__ void state_task(const int32_t* __restrict__ cu, int H
   // loop the last step of an iteration checks one chunk further for the
   // first step of the next, so that no wait for the producers sits at the
   // loop head (the compiler then drains every load in flight there too).
-  Ops<D, VT> bufA, bufB, bufC;
+  Ops<D, VT, QGB> bufA, bufB, bufC;
   if (nch > 0) {
     need_record(sy, slot0, H, h, 0, nch, l, upto, failed);
-    load_ops<D, VT>(bufA, rec_of(0), w, l, g, vt0);
+    load_ops<D, VT, QGB>(bufA, rec_of(0), w, l, g, vt0);
     if constexpr (NB == 3) {
       need_record(sy, slot0, H, h, 1, nch, l, upto, failed);
-      load_ops<D, VT>(bufB, rec_of(1), w, l, g, vt0);
+      load_ops<D, VT, QGB>(bufB, rec_of(1), w, l, g, vt0);
     }
     need_record(sy, slot0, H, h, NB - 1, nch, l, upto, failed);   // for the first step
   }
@@ -937,8 +985,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   int pair, vt;
   task_of<NV>(blockIdx.x, gridDim.x, pair, vt);
   if (pair >= N * H) return;
-  state_task<D, VT, 3, true>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt,
-                             Sync{nullptr, nullptr, nullptr}, lds);
+  state_task<D, VT, 3, true, false>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt,
+                                    Sync{nullptr, nullptr, nullptr}, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -975,6 +1023,11 @@ template <int VT>
 struct FusedState {
   static constexpr int NB = VT == 1 ? 3 : 2;
   static constexpr bool HOLD_SF = VT == 1;
+  // the shorter Qg / Bqk record where the prep is the longer leg (many
+  // (sequence, head) pairs); one-tile slices, chosen when the pass is the
+  // longer leg, keep Q' and (Bqk U)^T, whose read-out loads and multiplies
+  // less per step
+  static constexpr bool QGB = VT >= 2;
 };
 
 __global__ void clear_status_kernel(int* status) {
@@ -1017,8 +1070,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
       }
       __syncthreads();
     }
-    prep_item<D, SCALAR, RAW>(q, k, v, log_alpha, beta, H, h, t0, len, ws + ((size_t)slot * H + h) * Rec<D>::BYTES,
-                              lds, &hdr->status);
+    prep_item<D, SCALAR, RAW, FusedState<VT>::QGB>(q, k, v, log_alpha, beta, H, h, t0, len,
+                                                   ws + ((size_t)slot * H + h) * Rec<D>::BYTES, lds, &hdr->status);
     // publish: every wave's record stores acknowledged, then the flag
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1033,8 +1086,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void fused_kernel(
     task_of<NV>(task, nstate, pair, vt);
     const Sync sy{flags, &hdr->status, lead > 0 && vt == 0 ? flags : nullptr};
     if (pair < N * H)
-      state_task<D, VT, FusedState<VT>::NB, FusedState<VT>::HOLD_SF>(cu, H, init, fin, o, ws, sidx, pool_slots, pair / H,
-                                                                    pair % H, vt, sy, lds);
+      state_task<D, VT, FusedState<VT>::NB, FusedState<VT>::HOLD_SF, FusedState<VT>::QGB>(
+          cu, H, init, fin, o, ws, sidx, pool_slots, pair / H, pair % H, vt, sy, lds);
     if (tid == 0) sTicket = nstate + atomicAdd(&hdr->state_ticket, 1);
     __syncthreads();
     task = sTicket;
