@@ -64,14 +64,39 @@ TRAFFIC_SOURCES = ("kda_prefill_bf16.hip", "kda_decode.hip", "kda_backward.hip",
                    "kda_prefill_common.h")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one
+    space (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        ch = src[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and src[j] != ch:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest() -> str:
-    """sha256 of the sources of the kernels the traffic record covers, to tell
-    whether its counters still apply."""
+    """sha256 of the sources of the kernels the traffic record covers, their
+    comments and layout left out, to tell whether its counters still apply."""
     h = hashlib.sha256()
     for p in sorted(os.path.join(ROOT, "gated_delta_rule_88_amd", "csrc", f) for f in TRAFFIC_SOURCES):
-        with open(p, "rb") as fh:
+        with open(p, encoding="utf-8") as fh:
             h.update(os.path.basename(p).encode())
-            h.update(fh.read())
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -2,17 +2,19 @@
 //
 // Same chunk equations as kda_prefill.hip (derived from the recurrence of
 // the page "Kimi Delta Attention", §03, over chunks of C = 64 tokens, §06),
-// with the read-out regrouped so that the sequential pass needs no
-// intra-chunk product:
+// with the read-out in one of two groupings:
 //
 //   O = Qg S0 + Bqk E = Qg S0 + Bqk (U - W S0) = Q' S0 + Bqk U,
 //   Q' = Qg - Bqk W          (computed per chunk, in parallel)
 //
-// Kernel 1 (prep) runs one workgroup of four waves per (chunk, head) item,
-// two workgroups per CU, each wave holding 16 tokens of the chunk in
-// registers.  Per item it produces, as MFMA fragments:
-// W, Q' and Kc^T (fp16 fragments), U and (Bqk U)^T (fp16 accumulator tiles)
-// and e^G[C-1].
+// The second leaves the sequential pass no intra-chunk product; the first
+// leaves the per-chunk work less to do (the pass forms Bqk E from the E it
+// already holds), and is used where that work is the longer leg.
+//
+// The prep runs one workgroup of four waves per (chunk, head) item, two
+// workgroups per CU, each wave holding 16 tokens of the chunk in registers.
+// Per item it produces, as MFMA fragments: W, Kc^T and e^G[C-1]; U (fp16
+// accumulator tiles); and either Q' and (Bqk U)^T or Qg and Bqk.
 //
 // Precision (fp32 accumulation throughout).  Inside the prep, an operand
 // whose bf16 rounding would show in the outputs is split into hi + lo bf16
@@ -20,13 +22,13 @@
 // in Q K^T (the intra-chunk matrix Bqk), Bqk itself and U in Bqk U.  The
 // K K^T operands, T and Kg stay single bf16.  The decay-scaled operands
 // there span up to e^(+-80) (the anchor sits mid-chunk), which only bf16
-// covers.  The operands of the sequential pass -- W, Q', Kc, U, Bqk U, S and
-// E -- are all of moderate size and go through single fp16 (11-bit
-// significand).
+// covers.  The operands of the sequential pass -- W, Q' or Qg, Kc, U,
+// Bqk U or Bqk, S and E -- are all of moderate size and go through single
+// fp16 (11-bit significand).
 //
-// Kernel 2 (state pass) is one workgroup per (sequence, head, 16 value
-// columns): S's columns never mix in the recurrence.  Per chunk:
-//   E = U - W S;  O = Q' S + Bqk U;  S <- Diag(e^G[C-1]) S + Kc^T E.
+// The state pass is one task per (sequence, head, slice of value columns):
+// S's columns never mix in the recurrence.  Per chunk:
+//   E = U - W S;  O = Q' S + Bqk U (or Qg S + Bqk E);  S <- Diag(e^G[C-1]) S + Kc^T E.
 #include <algorithm>
 #include <cstddef>
 
@@ -85,7 +87,7 @@ template <int D>
 struct Rec {
   static constexpr int KB = D / 32, NT = D / 16;
   static constexpr size_t W = 0;                             // [4 token tiles][KB]          W
-  static constexpr size_t QP = W + 4 * KB * FB;              // [4 token tiles][KB]          Q'
+  static constexpr size_t QP = W + 4 * KB * FB;              // [4 token tiles][KB]          Q' (or Qg)
   static constexpr size_t KC = QP + 4 * KB * FB;             // [NT key tiles][2]            Kc^T
   static constexpr size_t U = KC + NT * 2 * FB;              // [NT value tiles][4 token tiles][64] f16x4
   static constexpr size_t BU = U + (size_t)NT * 4 * 64 * 8;  // same tiles of (Bqk U)^T: token l%16, columns 4 (l/16) + e
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void prep_kernel(
 // value tiles (16 VT columns) of S.  Wave w owns key rows [D/4 w, D/4 (w+1))
 // of the slice as accumulators and token tile w of every chunk; the operands
 // of the next two chunks are in flight while the current one is computed.
-// W, Q' and Kc serve every value tile of the slice, so a wider slice loads
+// W, Q' (or Qg) and Kc serve every value tile of the slice, so a wider slice loads
 // them once for more columns.
 // ---------------------------------------------------------------------------
 template <int D, int VT, bool QGB>

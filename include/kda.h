@@ -27,8 +27,11 @@
  *   it only enqueues kernels on `stream`
  *   (0 = the null stream), after reading the current device's compute-unit
  *   count and how many prefill workgroups a compute unit holds, which pick
- *   the launch shape of the bf16 prefill (the results are the same bit for
- *   bit either way).  Buffers must stay valid until that work is done.
+ *   the launch shape of the bf16 prefill (the final states are the same bit
+ *   for bit either way; the outputs may differ in their last bf16 place
+ *   between shapes, since slices of one value tile group the chunk read-out
+ *   differently from wider ones).  Buffers must stay valid until that work
+ *   is done.
  * - log_alpha is the natural logarithm of the decay gate alpha (fp32, <= 0):
  *   alpha_t[i] in (0, 1) decays key channel i (the per-channel gate of the
  *   "Kimi Linear Guide" page, section "2. Channel-Wise Data-Dependent

@@ -36,3 +36,13 @@ def test_backward_accounting():
     assert per_chunk == 32_505_856
     assert flops == 128 * 32 * per_chunk
     assert nbytes == 8192 * 32 * (3 * 256 + 512 + 2 + 256 + 4 * 512 + 4) + 2 * 32 * 128 * 128 * 4
+
+
+def test_traffic_record_key_ignores_comments_but_not_code():
+    src = 'int a = 1; // gate\n/* block\n   comment */ const char* s = "x // y /* z */";\nchar q = \'"\';  s += 1;\n'
+    stripped = bench.strip_comments(src)
+    assert stripped == 'int a = 1; const char* s = "x // y /* z */"; char q = \'"\'; s += 1;'
+    # comment edits and reflowing leave the key alone; a changed token does not
+    assert bench.strip_comments(src.replace("// gate", "// the gate, reworded").replace("  ", " ")) == stripped
+    assert bench.strip_comments(src.replace("a = 1", "a = 2")) != stripped
+    assert len(bench.source_digest()) == 16
