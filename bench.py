@@ -303,7 +303,12 @@ def _counter_pass(counter, part, outdir):
                 and r["Counter_Name"] == counter]
         if vals:
             out[key] = sum(vals) / len(vals)   # KiB per dispatch
-    return out, " ".join(cmd)
+    # recorded with the repository root and the output directory as $REPO and
+    # $OUT, and the interpreter by name
+    shown = [("$OUT" + a[len(outdir):]) if a.startswith(outdir) else
+             ("$REPO" + a[len(ROOT):]) if a.startswith(ROOT) else
+             "python3" if a == sys.executable else a for a in cmd]
+    return out, " ".join(shown)
 
 
 def run_traffic(outdir):
@@ -360,7 +365,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=("all", "prefill", "decode", "backward", "copy"), default="all")
-    ap.add_argument("--traffic", metavar="OUTDIR", nargs="?", const=os.path.join(ROOT, "gpurun_out", "traffic"))
+    ap.add_argument("--traffic", metavar="OUTDIR", nargs="?", const=os.path.join(ROOT, "profile_out", "traffic"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
