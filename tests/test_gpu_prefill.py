@@ -96,7 +96,8 @@ def test_state_pass_slice_widths(nseq, H):
     check(d, TOL[torch.bfloat16], f"state pass slice width, {nseq} x {H} pairs")
 
 
-def test_long_sequences_with_bounded_prep_lead():
+@pytest.mark.parametrize("D", [128, 64])
+def test_long_sequences_with_bounded_prep_lead(D):
     """two sequences of 70,000 and 66,000 tokens, 2 heads: sequences this long
     (64K tokens or more on average) make the bf16 prep wait whenever it runs
     more than a fixed number of chunks ahead of the state pass of its head;
@@ -104,14 +105,14 @@ def test_long_sequences_with_bounded_prep_lead():
     so the oracle on a column slice of v and of the initial state gives
     exactly those columns)"""
     lengths = [70000, 66000]
-    d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=497)
+    d = make_case(lengths, H=2, D=D, dtype=torch.bfloat16, seed=497 + (D == 64))
     o, f = run_gpu(d)
     cols = slice(32, 48)
     ro, rf = oracle.prefill(d["q"], d["k"], d["v"][..., cols], d["log_alpha"], d["beta"],
                             d["cu_seqlens"].long(), d["init_state"][:, :, cols, :])
     eo, es = row_rel_err(o[..., cols], ro), state_rel_err(f[:, :, cols, :], rf)
-    _log(f"long sequences, bounded prep lead: o {eo:.3e} state {es:.3e}")
-    record("two long sequences, bounded prep lead (cols 32..47)", eo, es, TOL[torch.bfloat16])
+    _log(f"long sequences, bounded prep lead, D={D}: o {eo:.3e} state {es:.3e}")
+    record(f"two long sequences, bounded prep lead, D={D} (cols 32..47)", eo, es, TOL[torch.bfloat16])
     assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
 
 
@@ -305,3 +306,13 @@ def test_prefill_then_decode_handoff():
     torch.cuda.synchronize()
     assert row_rel_err(torch.cat(outs), ro) <= 1e-4
     assert state_rel_err(state, rf) <= 1e-4
+
+
+@pytest.mark.parametrize("nseq,H", [(5, 3), (10, 4), (75, 4)], ids=["1-tile", "2-tile", "4-tile"])
+def test_state_pass_slice_widths_d64(nseq, H):
+    """as above with d = 64 (four value tiles per head): 15, 40 and 300
+    (sequence, head) pairs take slices of 1, 2 and 4 value tiles, the wider
+    two with the Qg / Bqk record; ragged lengths and random initial states"""
+    lengths = np.random.default_rng(530 + nseq).integers(1, 200, size=nseq).tolist()
+    d = make_case(lengths, H=H, D=64, dtype=torch.bfloat16, seed=531 + nseq)
+    check(d, TOL[torch.bfloat16], f"state pass slice width, d=64, {nseq} x {H} pairs")
