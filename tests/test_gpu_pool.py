@@ -51,6 +51,27 @@ def test_prefill_pooled(dtype, D, read_initial):
     assert torch.equal(after[untouched], pool[untouched])
 
 
+def test_prefill_pooled_wider_slices():
+    """12 sequences x 2 heads: the state pass takes two-value-tile slices (the
+    Qg / Bqk record), with states read from and written to scattered slots,
+    one sequence naming no slot"""
+    lengths = np.random.default_rng(77).integers(1, 300, size=12).tolist()
+    d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=78, init_std=0.0)
+    P = 20
+    idx = [17, 3, 9, -1, 0, 12, 5, 19, 8, 14, 2, 11]
+    pool = _pool(P, 2, 128, seed=79)
+    o, after = _prefill_pooled(d, idx, pool, read_initial=True)
+    init = torch.stack([pool[i] if i >= 0 else torch.zeros((2, 128, 128)) for i in idx])
+    ro, rf = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["cu_seqlens"].long(), init)
+    valid = [n for n, i in enumerate(idx) if i >= 0]
+    eo = row_rel_err(o, ro)
+    es = state_rel_err(after[[idx[n] for n in valid]], rf[valid])
+    print(f"pooled prefill, two-tile slices: o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+    untouched = [s for s in range(P) if s not in idx]
+    assert torch.equal(after[untouched], pool[untouched])
+
+
 def test_prefill_pooled_out_of_range_indices_are_skipped():
     lengths = [70, 130, 64]
     d = make_case(lengths, H=2, D=128, dtype=torch.bfloat16, seed=44, init_std=0.0)
